@@ -1,0 +1,178 @@
+"""Exact attention forward (FlashAttention) for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/attn.h`` (``libattn09.so``
+beside this file, built by ``exact_attention_09_amd.build``).  The functions
+here only marshal arguments: shapes, pointers, the stream.  Every step of the
+attention computation runs in the library's HIP kernels; there is no Python
+or CPU fallback.  Calling into the library without it being built raises.
+
+Names mirror the C entry points:
+
+* ``attn_fwd`` (bf16), ``attn_fwd_f32`` (fp32), ``attn_fwd_ex`` (either, with
+  split-KV options) take torch tensors on the GPU in BHSD layout and return
+  ``(o, lse)``;
+* ``attn_workspace_bytes``, ``attn_decode_num_splits``,
+  ``attn_status_string``, ``attn_last_error`` are the helpers.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn09.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ENOMEM, ATTN_EHIP = range(5)
+ATTN_BF16, ATTN_F32 = 0, 1
+ATTN_MAX_SPLITS = 256
+
+EXPORTED = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_workspace_bytes",
+            "attn_decode_num_splits", "attn_status_string", "attn_last_error")
+
+
+class AttnOpts(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"attn: {status_string(status)} ({status}): {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_attention_09_amd.build` "
+                           "(there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    fwd_args = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    for name in ("attn_fwd", "attn_fwd_f32"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = fwd_args
+    lib.attn_fwd_ex.restype = ctypes.c_int
+    lib.attn_fwd_ex.argtypes = fwd_args + [ctypes.c_int, ctypes.POINTER(AttnOpts)]
+    lib.attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_workspace_bytes.argtypes = [ctypes.c_int] * 4
+    lib.attn_decode_num_splits.restype = ctypes.c_int
+    lib.attn_decode_num_splits.argtypes = [ctypes.c_int] * 3
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def status_string(s: int) -> str:
+    return load_library().attn_status_string(int(s)).decode()
+
+
+attn_status_string = status_string
+
+
+def attn_last_error() -> str:
+    return load_library().attn_last_error().decode()
+
+
+def attn_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
+    return int(load_library().attn_workspace_bytes(B, H, d, num_splits))
+
+
+def attn_decode_num_splits(B: int, Hkv: int, Skv: int) -> int:
+    return int(load_library().attn_decode_num_splits(B, Hkv, Skv))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _shapes(q, k, cu_seqlens):
+    if cu_seqlens is not None:
+        if q.dim() == 3:
+            q, k = q.unsqueeze(0), k.unsqueeze(0)
+        if q.shape[0] != 1 or k.shape[0] != 1:
+            raise ValueError("varlen tensors have batch dimension 1")
+        B = cu_seqlens.numel() - 1
+        _, H, T, d = q.shape
+        _, Hkv, Tk, dk = k.shape
+        if Tk != T:
+            raise ValueError("varlen q and k must hold the same tokens")
+        return B, H, Hkv, T, T, d, dk
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("dense tensors are [B, H, S, d]")
+    B, H, Sq, d = q.shape
+    Bk, Hkv, Skv, dk = k.shape
+    if Bk != B:
+        raise ValueError("q and k batch sizes differ")
+    return B, H, Hkv, Sq, Skv, d, dk
+
+
+def attn_fwd_ex(q, k, v, o=None, lse=None, *, causal: bool = False, scale: float | None = None,
+                cu_seqlens=None, stream=None, dtype: int | None = None, num_splits: int = 0,
+                workspace=None, want_lse: bool = True):
+    """Run the forward pass through ``attn_fwd_ex``.
+
+    q [B,H,Sq,d], k/v [B,Hkv,Skv,d] (varlen: [1,H,T,d], [1,Hkv,T,d] with an
+    int32 ``cu_seqlens`` of B+1 prefix sums on the GPU).  ``o``/``lse`` are
+    allocated when not given (``lse`` only if ``want_lse``).  ``scale``
+    defaults to 1/sqrt(d).  ``stream`` defaults to torch's current stream.
+    Returns ``(o, lse)``.
+    """
+    import torch
+    lib = load_library()
+    B, H, Hkv, Sq, Skv, d, dk = _shapes(q, k, cu_seqlens)
+    if dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must have the shape [.., Hkv, Skv, d] with q's d")
+    if dtype is None:
+        dtype = {torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}.get(q.dtype)
+        if dtype is None:
+            raise ValueError(f"unsupported dtype {q.dtype}")
+    want = torch.bfloat16 if dtype == ATTN_BF16 else torch.float32
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != want or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous {want} tensor on the GPU")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise ValueError("cu_seqlens must be an int32 tensor on the GPU")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    opts = AttnOpts(int(num_splits), workspace.data_ptr() if workspace is not None else None,
+                    workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    st = lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Sq, Skv, d,
+                         float(scale), int(bool(causal)), _ptr(cu_seqlens), ctypes.c_void_p(stream),
+                         int(dtype), ctypes.byref(opts))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_last_error())
+    return o, lse
+
+
+def attn_fwd(q, k, v, o=None, lse=None, **kw):
+    """bf16 forward (``attn_fwd``); see ``attn_fwd_ex`` for the arguments."""
+    return attn_fwd_ex(q, k, v, o, lse, dtype=ATTN_BF16, **kw)
+
+
+def attn_fwd_f32(q, k, v, o=None, lse=None, **kw):
+    """fp32 forward (``attn_fwd_f32``); see ``attn_fwd_ex`` for the arguments."""
+    return attn_fwd_ex(q, k, v, o, lse, dtype=ATTN_F32, **kw)
+
+
+def raw_call(name: str, *args):
+    """Call a C entry point with already-marshalled arguments (used by the
+    ABI tests to drive the validation paths with raw pointers)."""
+    return getattr(load_library(), name)(*args)

@@ -1,0 +1,202 @@
+// C-ABI entry points: argument validation (before any HIP call), path
+// selection (tiled forward, split-KV decode, no-key fill) and the split
+// workspace.  See include/attn.h for the contract.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "attn.h"
+#include "attn_common.h"
+#include "attn_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+attn_status fail(attn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+attn_status hip_fail(hipError_t e, const char* what) {
+  return fail(ATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr size_t kWsAlign = 256;
+
+size_t ws_lse_offset(long rows, int d, int splits) {
+  const size_t o_bytes = (size_t)rows * splits * d * sizeof(float);
+  return (o_bytes + kWsAlign - 1) / kWsAlign * kWsAlign;
+}
+
+int env_splits() {
+  const char* e = getenv("ATTN_NUM_SPLITS");
+  if (e == nullptr || *e == '\0') return 0;
+  const int v = atoi(e);
+  return (v >= 1 && v <= ATTN_MAX_SPLITS) ? v : 0;
+}
+
+// Enough workgroups to cover the 256 CUs a few times over, chunks of at
+// least 256 keys.
+int heuristic_splits(int B, int Hkv, int Skv) {
+  const long base = (long)B * Hkv;
+  if (base <= 0 || Skv <= 0) return 1;
+  long want = (1024 + base - 1) / base;
+  long cap = Skv / 256;
+  if (cap < 1) cap = 1;
+  if (want > cap) want = cap;
+  if (want > ATTN_MAX_SPLITS) want = ATTN_MAX_SPLITS;
+  return want < 1 ? 1 : (int)want;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_EINVAL: return "invalid argument";
+    case ATTN_EUNSUPPORTED: return "unsupported configuration";
+    case ATTN_ENOMEM: return "out of memory";
+    case ATTN_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+size_t attn_workspace_bytes(int B, int H, int d, int num_splits) {
+  if (B < 0 || H < 0 || d <= 0 || num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return 0;
+  const long rows = (long)B * H;
+  return ws_lse_offset(rows, d, num_splits) + (size_t)rows * num_splits * sizeof(float);
+}
+
+int attn_decode_num_splits(int B, int Hkv, int Skv) {
+  const int e = env_splits();
+  return e > 0 ? e : heuristic_splits(B, Hkv, Skv);
+}
+
+attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int Hkv, int Sq, int Skv, int d, float scale, int causal,
+                        const int32_t* cu_seqlens, void* stream, attn_dtype dtype,
+                        const attn_opts* opts) {
+  g_err[0] = '\0';
+  // ---- validation: no HIP call until every check has passed
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return fail(ATTN_EINVAL, "unknown dtype %d", (int)dtype);
+  if (B < 0 || H < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || d < 0)
+    return fail(ATTN_EINVAL, "negative size (B=%d H=%d Hkv=%d Sq=%d Skv=%d d=%d)", B, H, Hkv, Sq, Skv, d);
+  if (opts != nullptr && (opts->num_splits < 0 || opts->num_splits > ATTN_MAX_SPLITS))
+    return fail(ATTN_EINVAL, "num_splits %d outside [0, %d]", opts->num_splits, ATTN_MAX_SPLITS);
+  if (B == 0 || H == 0 || Sq == 0) return ATTN_OK;  // nothing to compute
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+    return fail(ATTN_EINVAL, "q, k, v and o must not be NULL");
+  if (Hkv < 1 || H % Hkv != 0) return fail(ATTN_EINVAL, "H=%d is not a multiple of Hkv=%d", H, Hkv);
+  if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "head dim %d (built: 64, 128)", d);
+  if (!(std::isfinite(scale) && scale > 0.0f))
+    return fail(ATTN_EINVAL, "scale must be finite and > 0 (got %g)", (double)scale);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(ATTN_EINVAL, "q, k, v, o must be 16-byte aligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(ATTN_EINVAL, "lse must be 4-byte aligned");
+  const bool varlen = cu_seqlens != nullptr;
+  if (varlen) {
+    if (Sq != Skv) return fail(ATTN_EINVAL, "varlen needs Sq == Skv == total tokens (got %d, %d)", Sq, Skv);
+    if (!aligned(cu_seqlens, 4)) return fail(ATTN_EINVAL, "cu_seqlens must be 4-byte aligned");
+  }
+  // element counts must fit the 64-bit offsets and the 32-bit row counters
+  const long double q_elems = (long double)(varlen ? 1 : B) * H * Sq * d;
+  const long double kv_elems = (long double)(varlen ? 1 : B) * Hkv * Skv * d;
+  if (q_elems > 9.0e18L || kv_elems > 9.0e18L) return fail(ATTN_EINVAL, "tensor too large");
+
+  attn::Params p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.cu = cu_seqlens;
+  p.B = B; p.H = H; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv; p.d = d;
+  p.group = H / Hkv;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf16 = dtype == ATTN_BF16;
+
+  if (!varlen && Skv == 0) {
+    const hipError_t e = attn::launch_fill_empty(p, bf16, st);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "fill kernel");
+  }
+
+  const bool decode = !varlen && Sq == 1;
+  if (!decode) {
+    const int bm = bf16 ? attn::prefill_bf16_block_m() : attn::f32_block_m();
+    const long tiles = varlen ? (long)Sq / bm + B : attn::ceil_div(Sq, bm);
+    const long work = (varlen ? (long)H : (long)B * H) * tiles;
+    if (work > 0x7ffffff0L) return fail(ATTN_EINVAL, "too many query tiles");
+    p.tiles_per_head = (int)tiles;
+    p.work_items = (int)work;
+    const hipError_t e = bf16 ? attn::launch_prefill_bf16(p, st) : attn::launch_f32(p, false, st);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "forward kernel");
+  }
+
+  // ---- split-KV decode
+  int splits = (opts != nullptr && opts->num_splits > 0) ? opts->num_splits : attn_decode_num_splits(B, Hkv, Skv);
+  if (splits > Skv) splits = Skv;  // keep every split non-empty when possible
+  if (splits < 1) splits = 1;
+  p.num_splits = splits;
+  p.split_len = attn::ceil_div(Skv, splits);
+  p.tiles_per_head = 1;
+  if ((long)B * H * splits > 0x7ffffff0L) return fail(ATTN_EINVAL, "too many decode rows");
+  const size_t need = attn_workspace_bytes(B, H, d, splits);
+  const long rows = (long)B * H;
+  void* ws = nullptr;
+  bool own = false;
+  if (opts != nullptr && opts->workspace != nullptr) {
+    if (opts->workspace_bytes < need)
+      return fail(ATTN_EINVAL, "workspace of %zu bytes, %zu needed", opts->workspace_bytes, need);
+    if (!aligned(opts->workspace, kWsAlign)) return fail(ATTN_EINVAL, "workspace must be 256-byte aligned");
+    ws = opts->workspace;
+  } else {
+    const hipError_t e = hipMallocAsync(&ws, need, st);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(ATTN_ENOMEM, "workspace of %zu bytes: %s", need, hipGetErrorString(e));
+    }
+    own = true;
+  }
+  p.ws_o = (float*)ws;
+  p.ws_lse = (float*)((char*)ws + ws_lse_offset(rows, d, splits));
+
+  hipError_t e = bf16 ? attn::launch_decode_bf16(p, st) : attn::launch_f32(p, true, st);
+  attn_status status = ATTN_OK;
+  if (e != hipSuccess) {
+    status = hip_fail(e, "split kernel");
+  } else {
+    e = attn::launch_combine(p, bf16, st);
+    if (e != hipSuccess) status = hip_fail(e, "combine kernel");
+  }
+  if (own) {
+    const hipError_t ef = hipFreeAsync(ws, st);
+    if (ef != hipSuccess && status == ATTN_OK) status = hip_fail(ef, "workspace release");
+  }
+  return status;
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int Hkv, int Sq, int Skv, int d, float scale, int causal,
+                     const int32_t* cu_seqlens, void* stream) {
+  return attn_fwd_ex(q, k, v, o, lse, B, H, Hkv, Sq, Skv, d, scale, causal, cu_seqlens, stream,
+                     ATTN_BF16, nullptr);
+}
+
+attn_status attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int H, int Hkv, int Sq, int Skv, int d, float scale, int causal,
+                         const int32_t* cu_seqlens, void* stream) {
+  return attn_fwd_ex(q, k, v, o, lse, B, H, Hkv, Sq, Skv, d, scale, causal, cu_seqlens, stream,
+                     ATTN_F32, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+/*
+ * Exact attention forward (FlashAttention) for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI: plain pointers and sizes, no C++ types, no exceptions across the
+ * boundary.  Every pointer argument except `stream` points to device memory
+ * (HBM) unless stated otherwise.
+ *
+ * What is computed (per batch b, query head h, query row i):
+ *   S_ij = scale * q_i . k_j over the visible keys j,
+ *   P_ij = exp(S_ij - m_i) / l_i   (safe softmax, m_i = max_j S_ij),
+ *   O_i  = sum_j P_ij v_j,  LSE_i = m_i + ln l_i.
+ * The definition is section 1.1 of the TileLang tutorial chapter 15
+ * ("15-operators-attention"); the forward pass streams K/V tiles and keeps the
+ * running max and denominator (its section 2.3 recurrence), so the score
+ * matrix never reaches HBM.
+ *
+ * Layout (BHSD, contiguous, row-major; BHSD is the tutorial's section 1.1
+ * convention):
+ *   q, o : [B, H,   Sq,  d]        k, v : [B, Hkv, Skv, d]
+ *   lse  : [B, H,   Sq] fp32       (may be NULL: not written)
+ * q, k, v, o must be 16-byte aligned, lse 4-byte aligned.
+ *
+ * Grouped-query attention: H % Hkv == 0 and query head h reads KV head
+ * h / (H / Hkv) (tutorial section 4.8 (1)).  Hkv == 1 is multi-query.
+ *
+ * Causal masking is aligned to the bottom right: key j is visible to query i
+ * iff j <= i + (Skv - Sq) (tutorial section 3.4 (2) and 5.2).  A row that
+ * sees no key gets O = 0 and LSE = -inf (tutorial section 5.1 (2); the LSE
+ * value is this library's reading, the page leaves it open).
+ *
+ * Variable length (cu_seqlens != NULL; tutorial section 5.3): B is the number
+ * of sequences and the batch dimension is 1: q, o [1, H, T, d], k, v
+ * [1, Hkv, T, d], lse [1, H, T], with Sq == Skv == T.  cu_seqlens is a device
+ * array of B+1 int32 prefix sums (cu_seqlens[0] == 0, non-decreasing,
+ * cu_seqlens[B] == T).  Each sequence attends to itself only (Sq_b == Skv_b,
+ * so the causal offset is 0).  Values outside [0, T] are clamped by the
+ * kernels, so a malformed array gives wrong numbers, never an out-of-bounds
+ * access.
+ *
+ * Decode: a dense call with Sq == 1 takes the split-KV path (tutorial section
+ * 4.8 (3) and 5.4): the keys are cut into num_splits contiguous chunks of
+ * ceil(Skv / num_splits) keys (the last ones may be short or empty; the split
+ * count is clamped to Skv), each chunk produces a
+ * normalised partial output and a base-2 log-sum-exp, and a second kernel on
+ * the same stream combines them with weights l_s / sum l in a fixed split
+ * order (bitwise reproducible, no atomics).
+ *
+ * Precision: attn_fwd takes bf16 q/k/v/o; both products run on bf16 MFMA with
+ * fp32 accumulation, the probabilities are rounded to bf16 (round to nearest
+ * even) before the second product, the denominator is summed in fp32 before
+ * that rounding.  attn_fwd_f32 takes fp32 q/k/v/o and computes in fp32
+ * throughout (no low-precision step).
+ *
+ * Errors: arguments are validated on the host before any HIP call; on
+ * failure nothing is launched and no output is touched.  HIP failures give
+ * ATTN_EHIP.  attn_last_error() returns a per-thread message about the last
+ * failure.  Execution is asynchronous on `stream`: ATTN_OK means enqueued.
+ *
+ * Ownership: the caller owns every buffer and the stream; the library keeps
+ * no pointer after the call returns.  The only memory the library allocates
+ * is the split-KV workspace of the decode path when the caller passes none,
+ * taken and released stream-ordered (hipMallocAsync / hipFreeAsync) on
+ * `stream`.
+ *
+ * `stream` is a hipStream_t; NULL means the default stream.
+ */
+#ifndef EXACT_ATTENTION_09_ATTN_H
+#define EXACT_ATTENTION_09_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = 1,       /* invalid argument (null pointer, bad size, bad scale, ...) */
+  ATTN_EUNSUPPORTED = 2, /* valid but not built: d other than 64 or 128 */
+  ATTN_ENOMEM = 3,       /* the workspace could not be allocated */
+  ATTN_EHIP = 4          /* a HIP runtime call or a kernel launch failed */
+} attn_status;
+
+typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
+
+/* Largest split count the decode path accepts. */
+#define ATTN_MAX_SPLITS 256
+
+typedef struct {
+  /* Decode path only: 0 = library heuristic (or the ATTN_NUM_SPLITS
+   * environment variable when set), else 1 .. ATTN_MAX_SPLITS. */
+  int num_splits;
+  /* Decode path only: caller-provided device workspace of at least
+   * attn_workspace_bytes(...) bytes, 256-byte aligned; NULL lets the library
+   * allocate it stream-ordered.  The workspace must not be used by other work
+   * until this call's kernels on `stream` have finished. */
+  void* workspace;
+  size_t workspace_bytes;
+} attn_opts;
+
+/* bf16 q, k, v, o; fp32 lse.  The path named by the pages: tiled forward for
+ * Sq > 1 (or varlen), split-KV decode for dense Sq == 1. */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int Hkv, int Sq, int Skv, int d, float scale, int causal,
+                     const int32_t* cu_seqlens, void* stream);
+
+/* Same arguments with fp32 q, k, v, o. */
+attn_status attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int H, int Hkv, int Sq, int Skv, int d, float scale, int causal,
+                         const int32_t* cu_seqlens, void* stream);
+
+/* Same arguments plus the element type and options (opts may be NULL). */
+attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int Hkv, int Sq, int Skv, int d, float scale, int causal,
+                        const int32_t* cu_seqlens, void* stream, attn_dtype dtype,
+                        const attn_opts* opts);
+
+/* Bytes of workspace the decode path needs for B, H, d and num_splits
+ * (fp32 partial outputs [B,H,splits,d] and base-2 LSEs [B,H,splits]).
+ * Returns 0 for invalid sizes. */
+size_t attn_workspace_bytes(int B, int H, int d, int num_splits);
+
+/* The split count the decode path would use for these sizes when the caller
+ * passes none (the ATTN_NUM_SPLITS environment variable is honoured). */
+int attn_decode_num_splits(int B, int Hkv, int Skv);
+
+/* Static text for a status code. */
+const char* attn_status_string(attn_status s);
+
+/* Detail about the last failure on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_09_ATTN_H */

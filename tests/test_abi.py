@@ -1,0 +1,109 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, and rejects bad arguments before any HIP call."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import exact_attention_09_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ea.LIB_PATH):
+        from exact_attention_09_amd import build
+        build.build()
+    return ea.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_]\w*\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_entry_points():
+    assert set(declared_functions()) == set(ea.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+# fake, well-aligned device addresses: validation must reject before any use
+P = ctypes.c_void_p(0x100000)
+Q2 = ctypes.c_void_p(0x200000)
+
+
+def call(lib, *, q=P, k=P, v=P, o=Q2, lse=None, B=1, H=4, Hkv=2, Sq=8, Skv=8, d=64, scale=0.125,
+         causal=0, cu=None, dtype=0, opts=None):
+    return lib.attn_fwd_ex(q, k, v, o, lse, B, H, Hkv, Sq, Skv, d, scale, causal, cu, None, dtype,
+                           ctypes.byref(opts) if opts is not None else None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ea.ATTN_EINVAL),
+    (dict(o=None), ea.ATTN_EINVAL),
+    (dict(H=6, Hkv=4), ea.ATTN_EINVAL),
+    (dict(Hkv=0), ea.ATTN_EINVAL),
+    (dict(d=96), ea.ATTN_EUNSUPPORTED),
+    (dict(d=256), ea.ATTN_EUNSUPPORTED),
+    (dict(scale=0.0), ea.ATTN_EINVAL),
+    (dict(scale=-0.5), ea.ATTN_EINVAL),
+    (dict(scale=math.inf), ea.ATTN_EINVAL),
+    (dict(scale=math.nan), ea.ATTN_EINVAL),
+    (dict(B=-1), ea.ATTN_EINVAL),
+    (dict(Skv=-3), ea.ATTN_EINVAL),
+    (dict(q=ctypes.c_void_p(0x100008)), ea.ATTN_EINVAL),
+    (dict(lse=ctypes.c_void_p(0x300002)), ea.ATTN_EINVAL),
+    (dict(cu=ctypes.c_void_p(0x400000), Sq=8, Skv=9), ea.ATTN_EINVAL),
+    (dict(dtype=7), ea.ATTN_EINVAL),
+    (dict(opts=ea.AttnOpts(ea.ATTN_MAX_SPLITS + 1, None, 0)), ea.ATTN_EINVAL),
+    (dict(opts=ea.AttnOpts(-1, None, 0)), ea.ATTN_EINVAL),
+    # decode path with a caller workspace that is too small / misaligned
+    (dict(Sq=1, Skv=100, opts=ea.AttnOpts(4, 0x500000, 16)), ea.ATTN_EINVAL),
+    (dict(Sq=1, Skv=100, opts=ea.AttnOpts(4, 0x500010, 1 << 20)), ea.ATTN_EINVAL),
+])
+def test_rejects_before_any_hip_call(lib, kw, status):
+    assert call(lib, **kw) == status
+    assert ea.attn_last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Sq=0), dict(B=0, q=None, k=None, v=None, o=None)])
+def test_empty_problem_is_a_no_op(lib, kw):
+    assert call(lib, **kw) == ea.ATTN_OK
+
+
+def test_plain_entry_points_share_validation(lib):
+    for fn in (lib.attn_fwd, lib.attn_fwd_f32):
+        assert fn(P, P, P, Q2, None, 1, 4, 2, 8, 8, 96, 0.1, 0, None, None) == ea.ATTN_EUNSUPPORTED
+        assert fn(P, P, P, Q2, None, 0, 4, 2, 8, 8, 64, 0.1, 0, None, None) == ea.ATTN_OK
+
+
+def test_workspace_bytes(lib):
+    # [B,H,S,d] fp32 partial outputs (256-byte aligned) + [B,H,S] fp32 LSEs
+    assert ea.attn_workspace_bytes(32, 32, 128, 16) == 32 * 32 * 16 * 128 * 4 + 32 * 32 * 16 * 4
+    assert ea.attn_workspace_bytes(1, 1, 64, 3) == 768 + 12
+    assert ea.attn_workspace_bytes(1, 1, 64, 0) == 0
+    assert ea.attn_workspace_bytes(1, 1, 64, ea.ATTN_MAX_SPLITS + 1) == 0
+
+
+def test_decode_split_heuristic(lib, monkeypatch):
+    monkeypatch.delenv("ATTN_NUM_SPLITS", raising=False)
+    assert ea.attn_decode_num_splits(32, 8, 16384) == 4      # 256 (b, kv-head) pairs -> 1024 workgroups
+    assert ea.attn_decode_num_splits(1, 1, 100) == 1          # short caches are not split
+    assert ea.attn_decode_num_splits(1, 8, 1 << 20) == 128
+    monkeypatch.setenv("ATTN_NUM_SPLITS", "16")
+    assert ea.attn_decode_num_splits(32, 8, 16384) == 16
+
+
+def test_status_strings(lib):
+    assert ea.attn_status_string(ea.ATTN_OK) == "ok"
+    assert "unsupported" in ea.attn_status_string(ea.ATTN_EUNSUPPORTED)

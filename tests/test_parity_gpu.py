@@ -1,0 +1,307 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle on
+the same seeded inputs.
+
+Bars: |dO| <= 1e-5 for fp32 inputs; |dO| <= 1e-2 for bf16 inputs (where the
+exact output is >= 4 in magnitude, bf16 itself cannot represent it to 1e-2,
+so there the bar is half a bf16 spacing of the exact value plus 1e-2);
+|dLSE| <= 1e-3; rows that see no key must give O = 0 and LSE = -inf exactly.
+"""
+
+import math
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_attention_09_amd import synth
+from exact_attention_09_amd.workloads import WORKLOADS, Workload, host_f32, to_device
+from pins import assert_printed, golden
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_09_amd as ea
+    ea.load_library()  # fails loudly if the library was not built
+    return ea
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_run(q, k, v, dtype, causal, scale, cu=None, num_splits=0):
+    import exact_attention_09_amd as ea
+    qt, kt, vt = (to_device(x, dtype) for x in (q, k, v))
+    cut = torch.from_numpy(np.asarray(cu, np.int32)).cuda() if cu is not None else None
+    o, lse = ea.attn_fwd_ex(qt, kt, vt, causal=causal, scale=scale, cu_seqlens=cut,
+                            num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def bf16_half_spacing(x):
+    """Half the distance between adjacent bf16 values around |x|."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return 0.5 * 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def check(o, lse, o_ref, lse_ref, dtype, what=""):
+    o_ref = np.asarray(o_ref).reshape(o.shape)
+    lse_ref = np.asarray(lse_ref).reshape(lse.shape)
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), empty), f"{what}: -inf LSE pattern differs"
+    assert np.all(o[empty] == 0.0) if empty.any() else True
+    err = np.abs(o - o_ref)
+    if dtype == "f32":
+        tol = np.full_like(o_ref, 1e-5)
+    else:
+        tol = np.where(np.abs(o_ref) < 4.0, 1e-2, bf16_half_spacing(o_ref) + 1e-2)
+    worst = np.unravel_index(np.argmax(err - tol), err.shape)
+    assert np.all(err <= tol), (f"{what}: max |dO| {err.max():.3g} (at {worst}, ref {o_ref[worst]:.5g}, "
+                                f"got {o[worst]:.5g})")
+    fin = ~empty
+    lerr = np.abs(lse[fin] - lse_ref[fin]).max(initial=0.0)
+    assert lerr <= 1e-3, f"{what}: max |dLSE| {lerr:.3g}"
+    rounding = np.abs(o - o_ref).max(initial=0.0)
+    say(f"  {what}: max|dO|={rounding:.3g} max|dLSE|={lerr:.3g}")
+
+
+def oracle_dense(q, k, v, dtype, scale, causal, cu=None, rows=None):
+    return oracle.attention(host_f32(q, dtype), host_f32(k, dtype), host_f32(v, dtype), scale, causal,
+                            cu_seqlens=cu, rows=rows)
+
+
+# ------------------------------------------------------------ worked examples
+
+def _example_inputs(scores, d, rows):
+    n = len(scores)
+    q = np.zeros((1, 1, rows, d), np.float32)
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, n, d), np.float32)
+    k[0, 0, :, 0] = scores
+    v = np.zeros((1, 1, n, d), np.float32)
+    for j in range(n):
+        v[0, 0, j, j] = 1.0
+    return q, k, v
+
+
+@pytest.mark.parametrize("example", ["four_scores", "three_blocks"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,num_splits", [(1, 1), (1, 2), (1, 3), (2, 0), (130, 0)])
+def test_worked_examples_through_api(example, dtype, rows, num_splits):
+    """The pages' worked examples run through attn_fwd: q = e0, k_j = x_j e0,
+    v_j = e_j, scale 1, so O's first entries are the softmax weights.  One row
+    takes the split-KV path (2 splits of the four scores is the LLM course's
+    two-block example), more rows take the tiled path."""
+    g = golden()[example]
+    scores = [x for b in g["blocks"] for x in b]
+    q, k, v = _example_inputs(scores, 64, rows)
+    if dtype == "bf16":
+        q, k, v = (synth.f32_to_bf16_bits(x) for x in (q, k, v))  # all values exact in bf16
+    say(f"worked example {example} {dtype} rows={rows} splits={num_splits}")
+    o, lse = gpu_run(q, k, v, dtype, False, 1.0, num_splits=num_splits)
+    o_ref, lse_ref = oracle_dense(q, k, v, dtype, 1.0, False)
+    check(o, lse, o_ref, lse_ref, dtype, f"{example}/{dtype}")
+    for r in range(rows):
+        for j, w in enumerate(g["weights"]):
+            got = o[0, 0, r, j]
+            if dtype == "f32":
+                assert_printed(got, w, f"weight {j}")
+            else:  # bf16 output: printed value within its own rounding plus one bf16 spacing
+                assert abs(got - float(w)) <= 0.5 * 10 ** -(len(w.split('.')[1])) + 2 * bf16_half_spacing(got)
+        assert np.all(o[0, 0, r, len(scores):] == 0.0)
+    if example == "four_scores":
+        assert_printed(math.exp(lse[0, 0, 0]), g["exp_sum"], "sum of exp")
+
+
+# ------------------------------------------------------------ the workloads
+
+SAMPLE_ROWS = 384
+
+
+def sample_rows(wl: Workload, rng):
+    """Rows for the oracle at full size: tile edges and random rows."""
+    if wl.varlen:
+        rows = []
+        for b, L in enumerate(wl.lengths):
+            for i in sorted({0, 1, 127, 128, L // 2, L - 2, L - 1}):
+                if 0 <= i < L:
+                    rows.append((b, int(rng.integers(wl.H)), i))
+        while len(rows) < SAMPLE_ROWS:
+            b = int(rng.integers(len(wl.lengths)))
+            rows.append((b, int(rng.integers(wl.H)), int(rng.integers(wl.lengths[b]))))
+        return np.array(rows, np.int64)
+    fixed = sorted({0, 1, 63, 64, 127, 128, 129, wl.Sq // 2, wl.Sq - 129, wl.Sq - 128, wl.Sq - 2, wl.Sq - 1})
+    rows = [(int(rng.integers(wl.B)), int(rng.integers(wl.H)), i) for i in fixed if 0 <= i < wl.Sq]
+    while len(rows) < SAMPLE_ROWS:
+        rows.append((int(rng.integers(wl.B)), int(rng.integers(wl.H)), int(rng.integers(wl.Sq))))
+    return np.array(rows, np.int64)
+
+
+def gather_rows(wl, o, lse, rows):
+    if wl.varlen:
+        cu = wl.cu_seqlens()
+        return (np.stack([o[0, h, cu[b] + i] for b, h, i in rows]),
+                np.array([lse[0, h, cu[b] + i] for b, h, i in rows]))
+    return (np.stack([o[b, h, i] for b, h, i in rows]), np.array([lse[b, h, i] for b, h, i in rows]))
+
+
+FULL_ORACLE = {"single_head_f32", "mha_causal_s2048_d64", "decode_gqa_s16384_d128"}
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_parity(name):
+    wl = WORKLOADS[name]
+    say(f"workload {name}: B={wl.B} H={wl.H} Hkv={wl.Hkv} Sq={wl.Sq} Skv={wl.Skv} d={wl.d} "
+        f"{wl.dtype} causal={wl.causal}")
+    x = wl.make_inputs()
+    o, lse = gpu_run(x["q"], x["k"], x["v"], wl.dtype, wl.causal, wl.scale, cu=x["cu_seqlens"],
+                     num_splits=wl.num_splits)
+    # properties at full size
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    vmax = float(np.abs(host_f32(x["v"], wl.dtype)).max())
+    assert np.abs(o).max() <= vmax * (1 + 2 ** -7)  # a convex combination of V rows
+    if name in FULL_ORACLE:
+        o_ref, lse_ref = oracle_dense(x["q"], x["k"], x["v"], wl.dtype, wl.scale, wl.causal,
+                                      cu=x["cu_seqlens"])
+        check(o, lse, o_ref, lse_ref, wl.dtype, name)
+    else:
+        rows = sample_rows(wl, np.random.default_rng(wl.wid))
+        q, k, v = (host_f32(x[t], wl.dtype) for t in ("q", "k", "v"))
+        if wl.varlen:
+            q, k, v = q[0], k[0], v[0]
+        o_ref, lse_ref = oracle.attention(q, k, v, wl.scale, wl.causal, cu_seqlens=x["cu_seqlens"], rows=rows)
+        og, lg = gather_rows(wl, o, lse, rows)
+        check(og, lg, o_ref, lse_ref, wl.dtype, f"{name} ({len(rows)} sampled rows)")
+
+
+# ------------------------------------------------------------ edge shapes
+
+EDGE = [
+    # dtype, B, H, Hkv, Sq, Skv, d, causal, num_splits
+    ("bf16", 1, 2, 2, 100, 100, 64, False, 0),      # one partial tile
+    ("bf16", 1, 2, 2, 257, 257, 128, False, 0),     # ragged tail, several tiles
+    ("bf16", 2, 4, 1, 77, 200, 128, True, 0),       # Sq < Skv causal (bottom right), MQA
+    ("bf16", 1, 2, 2, 300, 130, 128, True, 0),      # Sq > Skv causal: 170 rows see nothing
+    ("bf16", 1, 2, 2, 300, 130, 64, True, 0),
+    ("bf16", 1, 3, 3, 129, 1, 64, False, 0),        # one key
+    ("bf16", 2, 6, 3, 200, 200, 64, True, 0),       # GQA group 2, d = 64
+    ("bf16", 1, 4, 4, 128, 0, 128, False, 0),       # no keys at all
+    ("bf16", 1, 2, 1, 1, 1000, 128, False, 0),      # decode, heuristic split
+    ("bf16", 2, 8, 2, 1, 333, 64, True, 3),         # decode d = 64 (causal is moot at Sq = 1)
+    ("bf16", 1, 4, 4, 1, 5, 128, False, 16),        # more splits than keys
+    ("bf16", 2, 40, 2, 1, 700, 128, False, 7),      # group of 20 heads: two head groups
+    ("bf16", 1, 2, 2, 1, 0, 64, False, 0),          # decode with an empty cache
+    ("f32", 1, 2, 2, 100, 100, 64, False, 0),
+    ("f32", 2, 4, 1, 77, 200, 128, True, 0),
+    ("f32", 1, 2, 2, 300, 130, 64, True, 0),
+    ("f32", 1, 2, 1, 1, 1000, 128, False, 0),
+    ("f32", 2, 6, 2, 1, 99, 64, False, 4),
+    ("f32", 1, 2, 2, 64, 0, 64, True, 0),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: "-".join(map(str, c)))
+def test_edge_shapes(case):
+    dtype, B, H, Hkv, Sq, Skv, d, causal, ns = case
+    say(f"edge case {case}")
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    q = synth.normal_tensor(seed * 10 + 0, (B, H, Sq, d), dtype)
+    k = synth.normal_tensor(seed * 10 + 1, (B, Hkv, Skv, d), dtype)
+    v = synth.normal_tensor(seed * 10 + 2, (B, Hkv, Skv, d), dtype)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = gpu_run(q, k, v, dtype, causal, scale, num_splits=ns)
+    o_ref, lse_ref = oracle_dense(q, k, v, dtype, scale, causal)
+    check(o, lse, o_ref, lse_ref, dtype, str(case))
+
+
+VARLEN_EDGE = [
+    ("bf16", (5, 0, 1, 127, 128, 129, 300), 4, 2, 128, True),
+    ("bf16", (5, 0, 1, 127, 128, 129, 300), 4, 4, 64, False),
+    ("bf16", (0,), 2, 1, 64, True),
+    ("bf16", (1000, 3), 8, 2, 128, True),
+    ("f32", (5, 0, 1, 33, 64, 100), 4, 2, 64, True),
+    ("f32", (70, 31), 2, 2, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_EDGE, ids=lambda c: "-".join(map(str, c)))
+def test_varlen_edges(case):
+    dtype, lengths, H, Hkv, d, causal = case
+    say(f"varlen case {case}")
+    T = sum(lengths)
+    cu = synth.cu_seqlens_from_lengths(lengths)
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    q = synth.normal_tensor(seed * 10 + 0, (1, H, T, d), dtype)
+    k = synth.normal_tensor(seed * 10 + 1, (1, Hkv, T, d), dtype)
+    v = synth.normal_tensor(seed * 10 + 2, (1, Hkv, T, d), dtype)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = gpu_run(q, k, v, dtype, causal, scale, cu=cu)
+    if T == 0:
+        return
+    o_ref, lse_ref = oracle.attention(host_f32(q, dtype)[0], host_f32(k, dtype)[0], host_f32(v, dtype)[0],
+                                      scale, causal, cu_seqlens=cu)
+    check(o[0], lse[0], o_ref, lse_ref, dtype, str(case))
+
+
+# ------------------------------------------------------------ determinism, canaries
+
+@pytest.mark.parametrize("Sq,ns", [(1, 16), (300, 0)])
+def test_bitwise_repeatable(Sq, ns):
+    import exact_attention_09_amd as ea
+    say(f"repeatability Sq={Sq} splits={ns}")
+    q = to_device(synth.normal_tensor(71, (2, 8, Sq, 128), "bf16"), "bf16")
+    k = to_device(synth.normal_tensor(72, (2, 2, 4000, 128), "bf16"), "bf16")
+    v = to_device(synth.normal_tensor(73, (2, 2, 4000, 128), "bf16"), "bf16")
+    o1, l1 = ea.attn_fwd(q, k, v, num_splits=ns)
+    o2, l2 = ea.attn_fwd(q, k, v, num_splits=ns)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype,Sq,causal", [("bf16", 200, True), ("bf16", 1, False), ("f32", 70, False),
+                                             ("f32", 1, False)])
+def test_guard_bands_untouched(dtype, Sq, causal):
+    """Outputs written through views inside larger buffers: the bytes around
+    them keep their canary values."""
+    import exact_attention_09_amd as ea
+    say(f"guard bands {dtype} Sq={Sq}")
+    B, H, Hkv, Skv, d = 2, 4, 2, 150, 64
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = to_device(synth.normal_tensor(81, (B, H, Sq, d), dtype), dtype)
+    k = to_device(synth.normal_tensor(82, (B, Hkv, Skv, d), dtype), dtype)
+    v = to_device(synth.normal_tensor(83, (B, Hkv, Skv, d), dtype), dtype)
+    n, pad = B * H * Sq * d, 256
+    obuf = torch.full((n + 2 * pad,), 7.0, dtype=tdt, device="cuda")
+    lbuf = torch.full((B * H * Sq + 2 * pad,), 9.0, dtype=torch.float32, device="cuda")
+    o = obuf[pad:pad + n].view(B, H, Sq, d)
+    lse = lbuf[pad:pad + B * H * Sq].view(B, H, Sq)
+    ea.attn_fwd_ex(q, k, v, o, lse, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[:pad] == 7.0) and torch.all(obuf[pad + n:] == 7.0)
+    assert torch.all(lbuf[:pad] == 9.0) and torch.all(lbuf[pad + B * H * Sq:] == 9.0)
+    assert torch.all(torch.isfinite(o.float()))
+
+
+def test_caller_workspace_matches_internal():
+    import exact_attention_09_amd as ea
+    say("caller workspace")
+    q = to_device(synth.normal_tensor(91, (3, 8, 1, 128), "bf16"), "bf16")
+    k = to_device(synth.normal_tensor(92, (3, 2, 2000, 128), "bf16"), "bf16")
+    v = to_device(synth.normal_tensor(93, (3, 2, 2000, 128), "bf16"), "bf16")
+    nbytes = ea.attn_workspace_bytes(3, 8, 128, 5)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    o1, l1 = ea.attn_fwd(q, k, v, num_splits=5)
+    o2, l2 = ea.attn_fwd(q, k, v, num_splits=5, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
