@@ -1,0 +1,213 @@
+"""Benchmark of the attention forward hot path on one MI355X.
+
+A step is one attn_fwd call over the headline workload (B=1, H=32,
+Sq=Skv=8192, d=128, bf16, non-causal), inputs resident in HBM.  The JSON line
+reports whole-job TFLOP/s (4*B*H*Sq*Skv*d flop per step), the prefill
+kernel's roofline (MFMA bf16 peak), the fp64 CPU oracle timed on a bounded
+sample of the same workload, and, under "workloads", the other shapes: the
+causal 8K run, the 2K d=64 causal run, varlen grouped-query prefill and
+split-KV decode (HBM roofline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
+METRIC = "attention fwd TFLOP/s (% bf16 MFMA peak) prefill; decode HBM GB/s (% peak)"
+HEADLINE = "mha_s8192_d128"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "exact_attention_09_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters for the current
+    kernel sources, or None when the summary is missing or stale."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_steps(fn, steps: int, warmup: int, stream):
+    """Warm up, then time `steps` calls: wall clock between two device
+    synchronisations, and per-launch HIP events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"wall_ms_per_step": 1e3 * wall / steps, "event_ms_mean": sum(per) / len(per),
+            "event_ms_median": per[len(per) // 2], "event_ms_min": per[0]}
+
+
+def run_workload(name: str, steps: int, warmup: int, inputs=None):
+    import numpy as np
+    import torch
+
+    import exact_attention_09_amd as ea
+    from exact_attention_09_amd.workloads import WORKLOADS, to_device
+    wl = WORKLOADS[name]
+    x = inputs if inputs is not None else wl.make_inputs()
+    q, k, v = (to_device(x[t], wl.dtype) for t in ("q", "k", "v"))
+    cu = torch.from_numpy(x["cu_seqlens"]).cuda() if x["cu_seqlens"] is not None else None
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    ws = None
+    ns = 0
+    if wl.Sq == 1 and not wl.varlen:
+        ns = wl.num_splits or ea.attn_decode_num_splits(wl.B, wl.Hkv, wl.Skv)
+        ws = torch.empty(ea.attn_workspace_bytes(wl.B, wl.H, wl.d, ns), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ea.attn_fwd_ex(q, k, v, o, lse, causal=wl.causal, scale=wl.scale, cu_seqlens=cu, num_splits=ns,
+                       workspace=ws, stream=stream.cuda_stream)
+
+    t = time_steps(step, steps, warmup, stream)
+    del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return wl, ns, t
+
+
+def cpu_baseline(name: str, inputs, target_s: float = 12.0):
+    """The oracle as it stands, on a bounded sample of query rows of the
+    same workload (every key of each sampled row), on the host cores."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_09_amd.workloads import WORKLOADS, host_f32
+    wl = WORKLOADS[name]
+    q, k, v = (host_f32(inputs[t], wl.dtype) for t in ("q", "k", "v"))
+    threads = max(1, min(16, os.cpu_count() or 1))
+
+    def rows_for(n):
+        idx = np.arange(n, dtype=np.int64) * 7919 % (wl.B * wl.H * wl.Sq)
+        return np.stack([idx // (wl.H * wl.Sq), (idx // wl.Sq) % wl.H, idx % wl.Sq], axis=1)
+
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, wl.scale, wl.causal, rows=rows_for(512), nthreads=threads)
+    cal = time.perf_counter() - t0
+    n = int(min(wl.B * wl.H * wl.Sq, max(512, 512 * target_s / max(cal, 1e-3))))
+    rows = rows_for(n)
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, wl.scale, wl.causal, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * n * wl.Skv * wl.d
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} query rows of {name} (all {wl.Skv} keys each, fp64 naive), {dt:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="headline workload only, no CPU baseline")
+    ap.add_argument("--workload", default=HEADLINE, help="time only this workload (profiling runs)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; the attention forward shards over "
+              "(batch, head) with no exchange, so there is no multi-GPU run to time", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import exact_attention_09_amd as ea
+    from exact_attention_09_amd.workloads import WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    ea.load_library()
+
+    if args.workload != HEADLINE:
+        wl, ns, t = run_workload(args.workload, args.steps, args.warmup)
+        print(json.dumps({"workload": args.workload, "timing": t}), flush=True)
+        return 0
+
+    wl = WORKLOADS[HEADLINE]
+    inputs = wl.make_inputs()
+    print(f"# timing {HEADLINE}", file=sys.stderr, flush=True)
+    _, _, t = run_workload(HEADLINE, args.steps, args.warmup, inputs)
+    flops = wl.flops()
+    value = flops / (t["wall_ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (t["event_ms_mean"] * 1e-3) / 1e12
+    traffic = read_traffic(HEADLINE)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t["wall_ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, "B": wl.B, "H": wl.H, "Hkv": wl.Hkv, "Sq": wl.Sq, "Skv": wl.Skv,
+                   "d": wl.d, "causal": wl.causal, "layout": "BHSD", "inputs": "N(0,1) seeded"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "prefill_bf16_kernel<128,64,false,false>",
+                     "launch_ms_mean": round(t["event_ms_mean"], 4),
+                     "launch_ms_median": round(t["event_ms_median"], 4)},
+    }
+    workloads = {}
+    if not args.quick:
+        for name in ("mha_causal_s8192_d128", "mha_causal_s2048_d64", "varlen_gqa_causal_d128",
+                     "decode_gqa_s16384_d128"):
+            print(f"# timing {name}", file=sys.stderr, flush=True)
+            w, ns, tt = run_workload(name, args.steps, args.warmup)
+            entry = {"ms_per_step": round(tt["wall_ms_per_step"], 4), "launch_ms_mean": round(tt["event_ms_mean"], 4)}
+            if w.Sq == 1 and not w.varlen:
+                gbps = w.bytes(ns) / (tt["event_ms_mean"] * 1e-3) / 1e9
+                entry.update({"GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+                              "num_splits": ns, "bytes_per_step": w.bytes(ns)})
+            else:
+                tf = w.flops() / (tt["event_ms_mean"] * 1e-3) / 1e12
+                entry.update({"TFLOP/s": round(tf, 2), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4),
+                              "flops_per_step": w.flops()})
+            workloads[name] = entry
+        print("# cpu baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(HEADLINE, inputs)
+    else:
+        line["cpu_baseline"] = None
+    line["workloads"] = workloads
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

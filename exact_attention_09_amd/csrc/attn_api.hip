@@ -96,8 +96,9 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
   if (opts != nullptr && (opts->num_splits < 0 || opts->num_splits > ATTN_MAX_SPLITS))
     return fail(ATTN_EINVAL, "num_splits %d outside [0, %d]", opts->num_splits, ATTN_MAX_SPLITS);
   if (B == 0 || H == 0 || Sq == 0) return ATTN_OK;  // nothing to compute
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
-    return fail(ATTN_EINVAL, "q, k, v and o must not be NULL");
+  if (q == nullptr || o == nullptr) return fail(ATTN_EINVAL, "q and o must not be NULL");
+  if (Skv > 0 && (k == nullptr || v == nullptr))
+    return fail(ATTN_EINVAL, "k and v must not be NULL when Skv > 0");
   if (Hkv < 1 || H % Hkv != 0) return fail(ATTN_EINVAL, "H=%d is not a multiple of Hkv=%d", H, Hkv);
   if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "head dim %d (built: 64, 128)", d);
   if (!(std::isfinite(scale) && scale > 0.0f))

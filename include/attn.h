@@ -18,7 +18,8 @@
  * convention):
  *   q, o : [B, H,   Sq,  d]        k, v : [B, Hkv, Skv, d]
  *   lse  : [B, H,   Sq] fp32       (may be NULL: not written)
- * q, k, v, o must be 16-byte aligned, lse 4-byte aligned.
+ * q, k, v, o must be 16-byte aligned, lse 4-byte aligned; k and v may be NULL
+ * when Skv == 0 (they are not read).
  *
  * Grouped-query attention: H % Hkv == 0 and query head h reads KV head
  * h / (H / Hkv) (tutorial section 4.8 (1)).  Hkv == 1 is multi-query.

@@ -51,6 +51,8 @@ def call(lib, *, q=P, k=P, v=P, o=Q2, lse=None, B=1, H=4, Hkv=2, Sq=8, Skv=8, d=
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), ea.ATTN_EINVAL),
     (dict(o=None), ea.ATTN_EINVAL),
+    (dict(k=None), ea.ATTN_EINVAL),
+    (dict(v=None, Sq=1), ea.ATTN_EINVAL),
     (dict(H=6, Hkv=4), ea.ATTN_EINVAL),
     (dict(Hkv=0), ea.ATTN_EINVAL),
     (dict(d=96), ea.ATTN_EUNSUPPORTED),

@@ -1,10 +1,12 @@
 """GPU parity: the HIP path through the C ABI against the fp64 CPU oracle on
 the same seeded inputs.
 
-Bars: |dO| <= 1e-5 for fp32 inputs; |dO| <= 1e-2 for bf16 inputs (where the
-exact output is >= 4 in magnitude, bf16 itself cannot represent it to 1e-2,
-so there the bar is half a bf16 spacing of the exact value plus 1e-2);
-|dLSE| <= 1e-3; rows that see no key must give O = 0 and LSE = -inf exactly.
+Bars: |dO| <= 1e-5 for fp32 inputs; for bf16 inputs the computation gets
+1e-2 and the final rounding of O to bf16 (the output format) is added on
+top: |dO| <= 1e-2 + half the bf16 spacing at the exact value (0.0039 or less
+for |O| < 2, 0.0078 for |O| in [2, 4)).  |dLSE| <= 1e-3.  Rows that see no
+key must give O = 0 and LSE = -inf exactly.  The printed max |dO| is the raw
+difference.
 """
 
 import math
@@ -65,7 +67,7 @@ def check(o, lse, o_ref, lse_ref, dtype, what=""):
     if dtype == "f32":
         tol = np.full_like(o_ref, 1e-5)
     else:
-        tol = np.where(np.abs(o_ref) < 4.0, 1e-2, bf16_half_spacing(o_ref) + 1e-2)
+        tol = 1e-2 + bf16_half_spacing(o_ref)
     worst = np.unravel_index(np.argmax(err - tol), err.shape)
     assert np.all(err <= tol), (f"{what}: max |dO| {err.max():.3g} (at {worst}, ref {o_ref[worst]:.5g}, "
                                 f"got {o[worst]:.5g})")
