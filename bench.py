@@ -143,6 +143,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline workload only, no CPU baseline")
     ap.add_argument("--workload", default=HEADLINE, help="time only this workload (profiling runs)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run one plain device copy of MIB MiB (scale for HBM byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; the attention forward shards over "
@@ -157,6 +159,17 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     ea.load_library()
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# calibration copy of {n} bytes done", file=sys.stderr, flush=True)
+        del src, dst
+        torch.cuda.empty_cache()
 
     if args.workload != HEADLINE:
         wl, ns, t = run_workload(args.workload, args.steps, args.warmup)

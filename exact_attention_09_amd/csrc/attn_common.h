@@ -103,6 +103,26 @@ __device__ inline bf16x8 to_bf16x8(float a0, float a1, float a2, float a3, float
 
 __device__ inline float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// Value of lane l ^ 32 combined with lane l's own, through v_permlane32_swap
+// (no LDS round trip): returns max / sum over the lane pair (l, l ^ 32).
+__device__ inline float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3).
+// Loads whose offset falls outside [0, bytes) return zero.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // ---------------------------------------------------------------- LDS swizzle
 //
 // A K or V tile sits in LDS row-major (one key per row, d contiguous) with

@@ -136,17 +136,21 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const Params p) {
     w_end = CAUSAL ? causal_kv_end(w_hi, off, skv) : skv;
   }
 
-  // ---- global -> register -> LDS tile loader (row-clamped tail)
+  // ---- global -> register -> LDS tile loader.  Buffer loads over the
+  // tile's valid rows: keys past skv read as zero (and are masked), the
+  // per-lane offset is the same for every tile, only the base moves.
   const int ld_c = tid % CH;
   const int ld_r = tid / CH;
+  const int ld_voff = ld_r * ROWB + ld_c * 16;
   u32x4 kreg[PASSES], vreg[PASSES];
   auto gload = [&](int k0) {
+    const int rows = skv - k0 < BN ? skv - k0 : BN;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + (int64_t)k0 * D, rows * ROWB);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + (int64_t)k0 * D, rows * ROWB);
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
-      int key = k0 + ld_r + RPP * i;
-      key = key < skv ? key : skv - 1;
-      kreg[i] = *(const u32x4*)(K + (int64_t)key * D + ld_c * 8);
-      vreg[i] = *(const u32x4*)(V + (int64_t)key * D + ld_c * 8);
+      kreg[i] = buffer_load16(kr, ld_voff, i * RPP * ROWB);
+      vreg[i] = buffer_load16(vr, ld_voff, i * RPP * ROWB);
     }
   };
   auto lstore = [&](int stage) {
@@ -179,6 +183,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const Params p) {
     gload(0);
     lstore(0);
   }
+  // Every global load issued so far (Q fragments, tile 0) completes here, so
+  // the loop body only ever waits for its own prefetch.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < nt; ++t) {
@@ -225,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const Params p) {
       for (int kbi = 0; kbi < NKB; ++kbi)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kbi][r]);
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      mx = pair32_max(mx);
 
       // lazy rescale: move the reference max only when P~ would exceed 2^tau
       const bool need = (mx > m_used) && ((mx - m_used) * sl2 > kTau);
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const Params p) {
   }
 
   // ---- epilogue: O = acc / l (0 for rows that saw no key), LSE natural log
-  const float l = l_part + shfl_xor_f(l_part, 32);
+  const float l = pair32_sum(l_part);
   if (qrow < sq) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     __bf16* orow = O + (int64_t)qrow * D;

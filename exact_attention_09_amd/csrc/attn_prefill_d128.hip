@@ -1,0 +1,368 @@
+// Tiled forward for bf16, d = 128, with matrix and vector phases of two wave
+// groups interleaved ("ping-pong"), gfx950.
+//
+// Same method as the basic tiled kernel (TileLang tutorial chapter 15,
+// sections 3.2 and 3.4; guards from section 5.1): one workgroup per query
+// tile, K/V tiles streamed through LDS, running max and denominator per row,
+// one division at the end.  The difference is how the work is laid on the CU.
+//
+// Per K/V tile a wave has two kinds of work: a matrix phase (the P~V MFMAs of
+// the previous tile and the QK^T MFMAs of this tile, 32 MFMAs) and a vector
+// phase (mask, row max, lazy rescale, exp2, row sum, bf16 conversion).  The
+// tutorial's pipelining discussion (section 3.3) and the FA-3 / FA-4 notes of
+// the CUDA course chapter 12 are about overlapping exactly these two.  Here
+// the overlap comes from the other wave on the same SIMD:
+//
+//   * 8 waves (512 threads), 32 query rows each, BM = 256.  Waves 0-3 form
+//     group A, waves 4-7 group B; wave w and wave w+4 share a SIMD.
+//   * Time is cut into slots by workgroup barriers.  In every slot one group
+//     runs its matrix phase while the other runs its vector phase; group B
+//     runs one slot behind group A, so the roles alternate every slot.
+//   * Each wave keeps a single S tile in registers (32 rows x 64 keys), so the
+//     register footprint is that of the plain loop (2 waves per SIMD).
+//   * K/V tiles (64 keys) live in a three-stage LDS ring (111 KB).  A tile is
+//     read during four consecutive slots (K by A then B, V by A then B two
+//     slots later); tile u is fetched from HBM two slots before it is written
+//     to LDS, and written after the barrier that ends the last read of the
+//     tile it replaces.
+//   * S^T = K Q^T and O^T = V^T P~^T on v_mfma_f32_32x32x16_bf16 (one query
+//     row per lane), K read with ds_read_b128, V with ds_read_b64_tr_b16.
+//     LDS rows are padded (K 272 B, V 320 B) so both reads are free of bank
+//     conflicts and every per-lane address is one register plus an immediate.
+//   * Lazy rescale (threshold 2^8), as in the basic kernel.
+#include "attn_common.h"
+#include "attn_internal.h"
+
+namespace attn {
+
+namespace {
+
+constexpr float kTau = 8.0f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(512, 2) void prefill_d128_kernel(const Params p) {
+  constexpr int D = 128;
+  constexpr int BN = 64;
+  constexpr int NW = 8;
+  constexpr int BM = 32 * NW;              // 256
+  constexpr int NT = 64 * NW;              // 512 threads
+  constexpr int ROWB = D * 2;
+  constexpr int CH = D / 8;                // 16-byte chunks per row
+  constexpr int KSTR = ROWB + 16;          // padded K row
+  constexpr int VSTR = ROWB + 64;          // padded V row
+  constexpr int KTILE_B = BN * KSTR;
+  constexpr int STAGE_B = BN * (KSTR + VSTR);
+  constexpr int STAGES = 3;
+  constexpr int RPP = NT / CH;             // 32 rows per load pass
+  constexpr int PASSES = BN / RPP;         // 2
+  constexpr int NKB = BN / 32;             // 2
+  constexpr int NDB = D / 32;              // 4
+  constexpr int NDC = D / 16;              // 8
+  constexpr int NKC = BN / 16;             // 4
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE_B];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int grp = wave >> 2;               // 0: group A, 1: group B (one slot behind)
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const float sl2 = p.scale_log2;
+
+  // ---- work item -> (b, h, query tile)
+  const int v = xcd_remap(blockIdx.x, p.work_items);
+  if (v < 0) return;
+  int h, tile, sq, skv, off;
+  int64_t q_row0, kv_row0;
+  if constexpr (!VARLEN) {
+    const int bh = v / p.tiles_per_head;
+    const int rank = v - bh * p.tiles_per_head;
+    tile = CAUSAL ? p.tiles_per_head - 1 - rank : rank;
+    const int b = bh / p.H;
+    h = bh - b * p.H;
+    sq = p.Sq;
+    skv = p.Skv;
+    off = skv - sq;
+    q_row0 = (int64_t)bh * sq;
+    kv_row0 = ((int64_t)b * p.Hkv + h / p.group) * skv;
+  } else {
+    h = v / p.tiles_per_head;
+    int vt = v - h * p.tiles_per_head;
+    if (CAUSAL) vt = p.tiles_per_head - 1 - vt;
+    const int T = p.Sq;
+    int acc = 0, start = 0;
+    tile = -1;
+    sq = 0;
+    for (int bb = 0; bb < p.B; ++bb) {
+      int s0 = p.cu[bb], s1 = p.cu[bb + 1];
+      s0 = s0 < 0 ? 0 : (s0 > T ? T : s0);
+      s1 = s1 < s0 ? s0 : (s1 > T ? T : s1);
+      const int nt = ceil_div(s1 - s0, BM);
+      if (vt < acc + nt) {
+        tile = vt - acc;
+        sq = s1 - s0;
+        start = s0;
+        break;
+      }
+      acc += nt;
+    }
+    if (tile < 0) return;
+    skv = sq;
+    off = 0;
+    q_row0 = (int64_t)h * T + start;
+    kv_row0 = (int64_t)(h / p.group) * T + start;
+  }
+
+  const __bf16* __restrict__ Q = (const __bf16*)p.q + q_row0 * D;
+  const __bf16* __restrict__ K = (const __bf16*)p.k + kv_row0 * D;
+  const __bf16* __restrict__ V = (const __bf16*)p.v + kv_row0 * D;
+  __bf16* __restrict__ O = (__bf16*)p.o + q_row0 * D;
+
+  const int q0 = tile * BM;
+  const int qw0 = q0 + 128 * grp + 32 * (wave & 3);
+  const int qrow = qw0 + l32;
+
+  // ---- Q fragments (B operand of S^T = K Q^T): row qrow, d = 16c + 8hh + j
+  bf16x8 qf[NDC];
+  if (qrow < sq) {
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) qf[c] = *(const bf16x8*)(Q + (int64_t)qrow * D + 16 * c + 8 * hh);
+  } else {
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) qf[c] = bf16x8{};
+  }
+
+  // ---- key ranges: the workgroup loads nt tiles, this wave computes nw
+  const int q_hi = q0 + BM < sq ? q0 + BM : sq;
+  const int kv_end = CAUSAL ? causal_kv_end(q_hi, off, skv) : skv;
+  const int nt = ceil_div(kv_end, BN);
+  int w_end = 0;
+  if (qw0 < sq) {
+    const int w_hi = qw0 + 32 < sq ? qw0 + 32 : sq;
+    w_end = CAUSAL ? causal_kv_end(w_hi, off, skv) : skv;
+  }
+  const int nw = ceil_div(w_end, BN);
+  // keys < lim are visible to this lane's row; kept as lim - 4hh so that the
+  // per-register key offset it is compared with stays wave-uniform
+  int lim = skv;
+  if (CAUSAL) {
+    const int c_lim = qrow + off + 1;
+    lim = c_lim < lim ? c_lim : lim;
+  }
+  const int lim_h = lim - 4 * hh;
+
+  // ---- loader: buffer loads (keys past skv read as zero) into the ring
+  const int ld_c = tid % CH;
+  const int ld_r = tid / CH;
+  const int ld_voff = ld_r * ROWB + ld_c * 16;
+  const int st_k = ld_r * KSTR + ld_c * 16;
+  const int st_v = KTILE_B + ld_r * VSTR + ld_c * 16;
+  u32x4 kreg[PASSES], vreg[PASSES];
+  auto gload = [&](int u) {
+    const int k0 = u * BN;
+    const int nrows = skv - k0 < BN ? skv - k0 : BN;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + (int64_t)k0 * D, nrows * ROWB);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + (int64_t)k0 * D, nrows * ROWB);
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+      kreg[i] = buffer_load16(kr, ld_voff, i * RPP * ROWB);
+      vreg[i] = buffer_load16(vr, ld_voff, i * RPP * ROWB);
+    }
+  };
+  auto lstore = [&](int u) {
+    unsigned char* sb = smem + (u % STAGES) * STAGE_B;
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+      *(u32x4*)(sb + st_k + i * RPP * KSTR) = kreg[i];
+      *(u32x4*)(sb + st_v + i * RPP * VSTR) = vreg[i];
+    }
+  };
+
+  // per-lane LDS offsets: K operand row l32, chunk hh (+32kb rows, +2c
+  // chunks); transposed V read at row 4(g>>1) + (t>>2), column
+  // 16(g&1) + 4(t&3) of a 16-lane group (g, t) (+16kc + 8e rows, +32db)
+  const int g16 = lane >> 4;
+  const int t16 = lane & 15;
+  const int k_lane = l32 * KSTR + 16 * hh;
+  const int v_lane = KTILE_B + (4 * (g16 >> 1) + (t16 >> 2)) * VSTR + (16 * (g16 & 1) + 4 * (t16 & 3)) * 2;
+
+  // ---- state
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  float m_used = -INFINITY;  // reference max (raw score units)
+  float neg_ms = 0.0f;       // -m_used * scale_log2 (0 while no key seen)
+  float l_part = 0.0f;       // this lane's share of the denominator
+  f32x16 s[NKB];             // S^T of the current tile
+  bf16x8 pb[NKC];            // P~ of the tile waiting for its P~V product
+
+  // ---- prologue: tiles 0..2 into the ring
+#pragma unroll
+  for (int u = 0; u < STAGES; ++u) {
+    if (u < nt) {
+      gload(u);
+      lstore(u);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int nslots = 2 * nt + 2;
+  for (int slot = 0; slot < nslots; ++slot) {
+    // HBM -> registers two slots ahead, registers -> LDS after the stage's
+    // previous tile has been read for the last time
+    if ((slot & 1) == 0) {
+      const int k = slot >> 1;
+      if (k >= 2 && k + 1 < nt) lstore(k + 1);
+      if (k >= 1 && k + 2 < nt) gload(k + 2);
+    }
+
+    const int ls = slot - grp;  // this group's own slot index
+    if (ls >= 0) {
+      const int t = ls >> 1;
+      if ((ls & 1) == 0) {
+        // matrix phase: P~V of tile t-1, then S^T of tile t.  Operand
+        // fragments are double buffered in registers: the LDS reads of step
+        // i+1 are in flight while the MFMAs of step i run.
+        const bool do_pv = t >= 1 && t - 1 < nw;
+        const bool do_qk = t < nw;
+        // the matrix phase issues first on this SIMD; the other group's
+        // vector work fills the issue slots the MFMAs leave free
+        __builtin_amdgcn_s_setprio(2);
+        const unsigned char* vb = smem + ((t + STAGES - 1) % STAGES) * STAGE_B + v_lane;
+        const unsigned char* kb = smem + (t % STAGES) * STAGE_B + k_lane;
+        auto vfrag = [&](int kc, int db) {
+          const s16x4 lo = lds_read_tr16(vb + 16 * kc * VSTR + 64 * db);
+          const s16x4 hi = lds_read_tr16(vb + (16 * kc + 8) * VSTR + 64 * db);
+          return join_tr(lo, hi);
+        };
+        auto kfrag = [&](int c, int kbi) { return *(const bf16x8*)(kb + kbi * 32 * KSTR + 32 * c); };
+        bf16x8 kf[2][NKB];
+        if (do_pv) {
+          bf16x8 vf[2][NDB];
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) vf[0][db] = vfrag(0, db);
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) {
+            if (kc + 1 < NKC) {
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) vf[(kc + 1) & 1][db] = vfrag(kc + 1, db);
+            } else if (do_qk) {
+#pragma unroll
+              for (int kbi = 0; kbi < NKB; ++kbi) kf[0][kbi] = kfrag(0, kbi);
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(vf[kc & 1][db], pb[kc], oacc[db]);
+          }
+        } else if (do_qk) {
+#pragma unroll
+          for (int kbi = 0; kbi < NKB; ++kbi) kf[0][kbi] = kfrag(0, kbi);
+        }
+        if (do_qk) {
+#pragma unroll
+          for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = f32x16{};
+#pragma unroll
+          for (int c = 0; c < NDC; ++c) {
+            if (c + 1 < NDC) {
+#pragma unroll
+              for (int kbi = 0; kbi < NKB; ++kbi) kf[(c + 1) & 1][kbi] = kfrag(c + 1, kbi);
+            }
+#pragma unroll
+            for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = mfma32(kf[c & 1][kbi], qf[c], s[kbi]);
+          }
+        }
+        __builtin_amdgcn_s_setprio(0);
+      } else if (t < nw) {
+        // vector phase for tile t
+        const int k0 = t * BN;
+        const bool partial = (k0 + BN > skv) || (CAUSAL && (k0 + BN - 1 > qw0 + off));
+        if (partial) {
+#pragma unroll
+          for (int kbi = 0; kbi < NKB; ++kbi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)  // key = k0 + 32kbi + 8(r/4) + 4hh + r%4
+              if (k0 + 32 * kbi + 8 * (r >> 2) + (r & 3) >= lim_h) s[kbi][r] = -INFINITY;
+        }
+        // row max and row sum as four independent partial chains
+        float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int kbi = 0; kbi < NKB; ++kbi)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[kbi][r]);
+        float mx = pair32_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+        const bool need = (mx > m_used) && ((mx - m_used) * sl2 > kTau);
+        if (__any(need)) {
+          const float m_new = need ? mx : m_used;
+          const float alpha = need ? fast_exp2((m_used - m_new) * sl2) : 1.0f;
+          l_part *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          m_used = m_new;
+          neg_ms = (m_used == -INFINITY) ? 0.0f : -m_used * sl2;
+        }
+        float rp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kbi = 0; kbi < NKB; ++kbi)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(fmaf(s[kbi][r], sl2, neg_ms));
+            s[kbi][r] = e;
+            rp[r & 3] += e;
+          }
+        l_part += (rp[0] + rp[1]) + (rp[2] + rp[3]);
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          const f32x16& sk = s[kc >> 1];
+          const int rb = 8 * (kc & 1);
+          pb[kc] = to_bf16x8(sk[rb + 0], sk[rb + 1], sk[rb + 2], sk[rb + 3], sk[rb + 4], sk[rb + 5],
+                             sk[rb + 6], sk[rb + 7]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l (0 for rows that saw no key), LSE natural log
+  const float l = pair32_sum(l_part);
+  if (qrow < sq) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    __bf16* orow = O + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        bf16x4 w;
+        w[0] = (__bf16)(oacc[db][4 * rg + 0] * inv);
+        w[1] = (__bf16)(oacc[db][4 * rg + 1] * inv);
+        w[2] = (__bf16)(oacc[db][4 * rg + 2] * inv);
+        w[3] = (__bf16)(oacc[db][4 * rg + 3] * inv);
+        *(bf16x4*)(orow + 32 * db + 8 * rg + 4 * hh) = w;
+      }
+    if (p.lse != nullptr && hh == 0)
+      p.lse[q_row0 + qrow] = l > 0.0f ? (m_used * sl2 + fast_log2(l)) * kLn2 : -INFINITY;
+  }
+}
+
+template <bool CAUSAL, bool VARLEN>
+hipError_t launch_one(const Params& p, hipStream_t st) {
+  const int grid = 8 * ceil_div(p.work_items, 8);
+  hipLaunchKernelGGL((prefill_d128_kernel<CAUSAL, VARLEN>), dim3(grid), dim3(512), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_d128_block_m() { return 256; }
+
+hipError_t launch_prefill_d128(const Params& p, hipStream_t st) {
+  if (p.work_items <= 0) return hipSuccess;
+  const bool var = p.cu != nullptr;
+  if (p.causal) return var ? launch_one<true, true>(p, st) : launch_one<true, false>(p, st);
+  return var ? launch_one<false, true>(p, st) : launch_one<false, false>(p, st);
+}
+
+}  // namespace attn
