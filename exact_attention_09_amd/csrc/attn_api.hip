@@ -133,16 +133,18 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
 
   const bool decode = !varlen && Sq == 1;
   if (!decode) {
-    const bool pipelined = bf16 && d == 128 && getenv("ATTN_BASIC_PREFILL") == nullptr;
+    // d = 64 stays on the basic kernel: its 4-wave workgroups fit several per
+    // CU, and at half the MFMA work per tile the vector work sets the pace
+    const bool pingpong = bf16 && d == 128 && getenv("ATTN_BASIC_PREFILL") == nullptr;
     const int bm = !bf16 ? attn::f32_block_m()
-                         : (pipelined ? attn::prefill_d128_block_m() : attn::prefill_bf16_block_m());
+                         : (pingpong ? attn::prefill_pp_block_m() : attn::prefill_bf16_block_m());
     const long tiles = varlen ? (long)Sq / bm + B : attn::ceil_div(Sq, bm);
     const long work = (varlen ? (long)H : (long)B * H) * tiles;
     if (work > 0x7ffffff0L) return fail(ATTN_EINVAL, "too many query tiles");
     p.tiles_per_head = (int)tiles;
     p.work_items = (int)work;
     const hipError_t e = !bf16 ? attn::launch_f32(p, false, st)
-                               : (pipelined ? attn::launch_prefill_d128(p, st) : attn::launch_prefill_bf16(p, st));
+                               : (pingpong ? attn::launch_prefill_pp(p, st) : attn::launch_prefill_bf16(p, st));
     return e == hipSuccess ? ATTN_OK : hip_fail(e, "forward kernel");
   }
 

@@ -11,9 +11,9 @@ namespace attn {
 int prefill_bf16_block_m();
 hipError_t launch_prefill_bf16(const Params& p, hipStream_t st);
 
-// bf16 tiled forward, d = 128, software pipelined (BM = 256).
-int prefill_d128_block_m();
-hipError_t launch_prefill_d128(const Params& p, hipStream_t st);
+// bf16 tiled forward, two wave groups in ping-pong (BM = 256), d = 128.
+int prefill_pp_block_m();
+hipError_t launch_prefill_pp(const Params& p, hipStream_t st);
 
 // fp32 forward (VALU); with split set it writes decode partials instead.
 int f32_block_m();

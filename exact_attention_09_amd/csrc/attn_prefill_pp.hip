@@ -1,4 +1,4 @@
-// Tiled forward for bf16, d = 128, with matrix and vector phases of two wave
+// Tiled forward for bf16 (d = 128), with matrix and vector phases of two wave
 // groups interleaved ("ping-pong"), gfx950.
 //
 // Same method as the basic tiled kernel (TileLang tutorial chapter 15,
@@ -7,7 +7,7 @@
 // one division at the end.  The difference is how the work is laid on the CU.
 //
 // Per K/V tile a wave has two kinds of work: a matrix phase (the P~V MFMAs of
-// the previous tile and the QK^T MFMAs of this tile, 32 MFMAs) and a vector
+// the previous tile and the QK^T MFMAs of this tile, d/4 MFMAs) and a vector
 // phase (mask, row max, lazy rescale, exp2, row sum, bf16 conversion).  The
 // tutorial's pipelining discussion (section 3.3) and the FA-3 / FA-4 notes of
 // the CUDA course chapter 12 are about overlapping exactly these two.  Here
@@ -20,15 +20,20 @@
 //     runs one slot behind group A, so the roles alternate every slot.
 //   * Each wave keeps a single S tile in registers (32 rows x 64 keys), so the
 //     register footprint is that of the plain loop (2 waves per SIMD).
-//   * K/V tiles (64 keys) live in a three-stage LDS ring (111 KB).  A tile is
+//   * K/V tiles (64 keys) live in a three-stage LDS ring (111 KB at d = 128,
+//     64.5 KB at d = 64, so two workgroups share a CU either way).  A tile is
 //     read during four consecutive slots (K by A then B, V by A then B two
 //     slots later); tile u is fetched from HBM two slots before it is written
 //     to LDS, and written after the barrier that ends the last read of the
 //     tile it replaces.
 //   * S^T = K Q^T and O^T = V^T P~^T on v_mfma_f32_32x32x16_bf16 (one query
 //     row per lane), K read with ds_read_b128, V with ds_read_b64_tr_b16.
-//     LDS rows are padded (K 272 B, V 320 B) so both reads are free of bank
-//     conflicts and every per-lane address is one register plus an immediate.
+//     LDS rows are padded (K by 16 B, V by 64 B) so both reads are free of
+//     bank conflicts at d = 64 and 128 and every per-lane address is one
+//     register plus an immediate.
+//   * In steady state the P~V and QK^T MFMAs of a matrix phase (equal in
+//     number, d/8 each) are issued alternately, with their operand reads
+//     pinned a few MFMAs ahead.
 //   * Lazy rescale (threshold 2^8), as in the basic kernel.
 #include "attn_common.h"
 #include "attn_internal.h"
@@ -40,10 +45,16 @@ namespace {
 constexpr float kTau = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
-template <bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(512, 2) void prefill_d128_kernel(const Params p) {
-  constexpr int D = 128;
-  constexpr int BN = 64;
+#ifndef ATTN_PP_BN
+#define ATTN_PP_BN 64
+#endif
+#ifndef ATTN_PP_PRIO
+#define ATTN_PP_PRIO 2
+#endif
+
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
+  constexpr int BN = ATTN_PP_BN;
   constexpr int NW = 8;
   constexpr int BM = 32 * NW;              // 256
   constexpr int NT = 64 * NW;              // 512 threads
@@ -56,10 +67,14 @@ __global__ __launch_bounds__(512, 2) void prefill_d128_kernel(const Params p) {
   constexpr int STAGES = 3;
   constexpr int RPP = NT / CH;             // 32 rows per load pass
   constexpr int PASSES = BN / RPP;         // 2
+  static_assert(PASSES >= 1 && BN % RPP == 0, "tile must be a whole number of load passes");
   constexpr int NKB = BN / 32;             // 2
   constexpr int NDB = D / 32;              // 4
   constexpr int NDC = D / 16;              // 8
   constexpr int NKC = BN / 16;             // 4
+  constexpr int NPV = NKC * NDB;           // P~V MFMAs per tile
+  constexpr int NQK = NDC * NKB;           // QK^T MFMAs per tile
+  static_assert(NPV == NQK, "the fused matrix phase pairs one P~V and one QK^T MFMA");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE_B];
 
@@ -230,7 +245,7 @@ __global__ __launch_bounds__(512, 2) void prefill_d128_kernel(const Params p) {
         const bool do_qk = t < nw;
         // the matrix phase issues first on this SIMD; the other group's
         // vector work fills the issue slots the MFMAs leave free
-        __builtin_amdgcn_s_setprio(2);
+        __builtin_amdgcn_s_setprio(ATTN_PP_PRIO);
         const unsigned char* vb = smem + ((t + STAGES - 1) % STAGES) * STAGE_B + v_lane;
         const unsigned char* kb = smem + (t % STAGES) * STAGE_B + k_lane;
         auto vfrag = [&](int kc, int db) {
@@ -239,6 +254,30 @@ __global__ __launch_bounds__(512, 2) void prefill_d128_kernel(const Params p) {
           return join_tr(lo, hi);
         };
         auto kfrag = [&](int c, int kbi) { return *(const bf16x8*)(kb + kbi * 32 * KSTR + 32 * c); };
+        if (do_pv && do_qk) {
+          // steady state: the 16 P~V and 16 QK^T MFMAs are independent, so
+          // they are issued alternately, each with its operand read a few
+          // MFMAs ahead (order pinned with sched_group_barrier: 0x100 LDS
+          // read, 0x008 MFMA)
+#pragma unroll
+          for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = f32x16{};
+#pragma unroll
+          for (int i = 0; i < NPV; ++i) {
+            const int kc = i / NDB, db = i % NDB;
+            oacc[db] = mfma32(vfrag(kc, db), pb[kc], oacc[db]);
+            const int c = i / NKB, kbi = i % NKB;
+            s[kbi] = mfma32(kfrag(c, kbi), qf[c], s[kbi]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
+#pragma unroll
+          for (int i = 0; i < NPV - 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        } else {
         bf16x8 kf[2][NKB];
         if (do_pv) {
           bf16x8 vf[2][NDB];
@@ -272,6 +311,7 @@ __global__ __launch_bounds__(512, 2) void prefill_d128_kernel(const Params p) {
 #pragma unroll
             for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = mfma32(kf[c & 1][kbi], qf[c], s[kbi]);
           }
+        }
         }
         __builtin_amdgcn_s_setprio(0);
       } else if (t < nw) {
@@ -347,22 +387,28 @@ __global__ __launch_bounds__(512, 2) void prefill_d128_kernel(const Params p) {
   }
 }
 
-template <bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_one(const Params& p, hipStream_t st) {
   const int grid = 8 * ceil_div(p.work_items, 8);
-  hipLaunchKernelGGL((prefill_d128_kernel<CAUSAL, VARLEN>), dim3(grid), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((prefill_pp_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(512), 0, st, p);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const Params& p, hipStream_t st) {
+  const bool var = p.cu != nullptr;
+  if (p.causal) return var ? launch_one<D, true, true>(p, st) : launch_one<D, true, false>(p, st);
+  return var ? launch_one<D, false, true>(p, st) : launch_one<D, false, false>(p, st);
 }
 
 }  // namespace
 
-int prefill_d128_block_m() { return 256; }
+int prefill_pp_block_m() { return 256; }
 
-hipError_t launch_prefill_d128(const Params& p, hipStream_t st) {
+hipError_t launch_prefill_pp(const Params& p, hipStream_t st) {
   if (p.work_items <= 0) return hipSuccess;
-  const bool var = p.cu != nullptr;
-  if (p.causal) return var ? launch_one<true, true>(p, st) : launch_one<true, false>(p, st);
-  return var ? launch_one<false, true>(p, st) : launch_one<false, false>(p, st);
+  if (p.d != 128) return hipErrorInvalidValue;
+  return launch_d<128>(p, st);
 }
 
 }  // namespace attn

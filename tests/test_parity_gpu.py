@@ -256,6 +256,41 @@ def test_varlen_edges(case):
     check(o[0], lse[0], o_ref, lse_ref, dtype, str(case))
 
 
+BASIC_D128 = [
+    ("dense", 1, 2, 2, 257, 257, True),
+    ("dense", 2, 4, 1, 77, 200, True),
+    ("dense", 1, 2, 2, 300, 130, False),
+    ("varlen", (5, 0, 127, 128, 300), 4, 2, 0, 0, True),
+]
+
+
+@pytest.mark.parametrize("case", BASIC_D128, ids=lambda c: "-".join(map(str, c)))
+def test_basic_kernel_d128(case, monkeypatch):
+    """d = 128 prefill normally runs the ping-pong kernel; ATTN_BASIC_PREFILL
+    selects the basic tiled kernel, which must meet the same bar."""
+    monkeypatch.setenv("ATTN_BASIC_PREFILL", "1")
+    say(f"basic d128 case {case}")
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    d, scale = 128, 1.0 / math.sqrt(128)
+    if case[0] == "varlen":
+        _, lengths, H, Hkv, _, _, causal = case
+        T = sum(lengths)
+        cu = synth.cu_seqlens_from_lengths(lengths)
+        q, k, v = (synth.normal_tensor(seed * 10 + i, (1, h, T, d), "bf16") for i, h in enumerate((H, Hkv, Hkv)))
+        o, lse = gpu_run(q, k, v, "bf16", causal, scale, cu=cu)
+        o_ref, lse_ref = oracle.attention(host_f32(q, "bf16")[0], host_f32(k, "bf16")[0],
+                                          host_f32(v, "bf16")[0], scale, causal, cu_seqlens=cu)
+        check(o[0], lse[0], o_ref, lse_ref, "bf16", str(case))
+        return
+    _, B, H, Hkv, Sq, Skv, causal = case
+    q = synth.normal_tensor(seed * 10 + 0, (B, H, Sq, d), "bf16")
+    k = synth.normal_tensor(seed * 10 + 1, (B, Hkv, Skv, d), "bf16")
+    v = synth.normal_tensor(seed * 10 + 2, (B, Hkv, Skv, d), "bf16")
+    o, lse = gpu_run(q, k, v, "bf16", causal, scale)
+    o_ref, lse_ref = oracle_dense(q, k, v, "bf16", scale, causal)
+    check(o, lse, o_ref, lse_ref, "bf16", str(case))
+
+
 # ------------------------------------------------------------ determinism, canaries
 
 @pytest.mark.parametrize("Sq,ns", [(1, 16), (300, 0)])
