@@ -8,7 +8,7 @@
 //
 // Per K/V tile a wave has two kinds of work: a matrix phase (the P~V MFMAs of
 // the previous tile and the QK^T MFMAs of this tile, d/4 MFMAs) and a vector
-// phase (mask, row max, lazy rescale, exp2, row sum, bf16 conversion).  The
+// phase (mask, exp2 against the reference max, row sum, bf16 conversion).  The
 // tutorial's pipelining discussion (section 3.3) and the FA-3 / FA-4 notes of
 // the CUDA course chapter 12 are about overlapping exactly these two.  Here
 // the overlap comes from the other wave on the same SIMD:
@@ -20,21 +20,28 @@
 //     runs one slot behind group A, so the roles alternate every slot.
 //   * Each wave keeps a single S tile in registers (32 rows x 64 keys), so the
 //     register footprint is that of the plain loop (2 waves per SIMD).
-//   * K/V tiles (64 keys) live in a three-stage LDS ring (111 KB at d = 128,
-//     64.5 KB at d = 64, so two workgroups share a CU either way).  A tile is
-//     read during four consecutive slots (K by A then B, V by A then B two
-//     slots later); tile u is fetched from HBM two slots before it is written
-//     to LDS, and written after the barrier that ends the last read of the
-//     tile it replaces.
+//   * K/V tiles (64 keys) live in a four-stage LDS ring (128 KB).  A tile
+//     is read during four consecutive slots (K by A then B, V by A then B
+//     two slots later).  Tiles go from HBM straight to LDS (buffer_load ...
+//     lds, no registers on the way), laid out in MFMA fragment order; tile u
+//     is fetched in slot 2u-4 into the stage of tile u-4, after the barrier
+//     that ends that tile's last read, and waited for at the end of slot
+//     2u-1.
 //   * S^T = K Q^T and O^T = V^T P~^T on v_mfma_f32_32x32x16_bf16 (one query
 //     row per lane), K read with ds_read_b128, V with ds_read_b64_tr_b16.
-//     LDS rows are padded (K by 16 B, V by 64 B) so both reads are free of
-//     bank conflicts at d = 64 and 128 and every per-lane address is one
-//     register plus an immediate.
+//     Each fragment read covers one contiguous block (1 KB or 512 B), so it
+//     is free of bank conflicts and its address is one register plus an
+//     immediate.
 //   * In steady state the P~V and QK^T MFMAs of a matrix phase (equal in
 //     number, d/8 each) are issued alternately, with their operand reads
 //     pinned a few MFMAs ahead.
-//   * Lazy rescale (threshold 2^8), as in the basic kernel.
+//   * Reference max without a per-tile max: P~ = exp2(S scale' - m scale')
+//     against the current reference m, S kept in registers.  If some lane's
+//     share of a row's tile sum exceeds 2^8 (so some P~ > 2^8), or a row has
+//     no reference yet, the tile takes a rare path: exact row max, m <-
+//     max(m, rowmax), O and l scaled by exp2((m_old - m_new) scale'), P~
+//     again.  P~ stays <= 2^8 as with the lazy rescale of the basic kernel,
+//     which instead compares the tile max with m every tile.
 #include "attn_common.h"
 #include "attn_internal.h"
 
@@ -42,7 +49,7 @@ namespace attn {
 
 namespace {
 
-constexpr float kTau = 8.0f;
+constexpr float kSumCap = 256.0f;  // 2^8: bound on a lane's share of a tile row sum
 constexpr float kLn2 = 0.69314718055994530942f;
 
 #ifndef ATTN_PP_BN
@@ -51,6 +58,32 @@ constexpr float kLn2 = 0.69314718055994530942f;
 #ifndef ATTN_PP_PRIO
 #define ATTN_PP_PRIO 2
 #endif
+#ifndef ATTN_PP_AHEAD
+#define ATTN_PP_AHEAD 3
+#endif
+
+#pragma clang diagnostic push
+// m0 is written by these loads only; no other instruction in the kernel reads it
+#pragma clang diagnostic ignored "-Winline-asm"
+// HBM -> LDS without registers: 16 bytes per lane at LDS address m0 + 16 *
+// lane (out-of-range bytes arrive as zeros).  Issued as inline assembly so
+// that the compiler, which cannot tell the ring stages apart, does not wait
+// for these loads before every LDS read; the kernel waits for them itself
+// (vmcnt) before the barrier that publishes a stage.  lds_addr must be
+// wave-uniform.
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, int voff, int soff, unsigned lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(soff), "s"(lds_addr)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ inline unsigned lds_u32(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
 
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
@@ -58,16 +91,10 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   constexpr int NW = 8;
   constexpr int BM = 32 * NW;              // 256
   constexpr int NT = 64 * NW;              // 512 threads
-  constexpr int ROWB = D * 2;
-  constexpr int CH = D / 8;                // 16-byte chunks per row
-  constexpr int KSTR = ROWB + 16;          // padded K row
-  constexpr int VSTR = ROWB + 64;          // padded V row
-  constexpr int KTILE_B = BN * KSTR;
-  constexpr int STAGE_B = BN * (KSTR + VSTR);
-  constexpr int STAGES = 3;
-  constexpr int RPP = NT / CH;             // 32 rows per load pass
-  constexpr int PASSES = BN / RPP;         // 2
-  static_assert(PASSES >= 1 && BN % RPP == 0, "tile must be a whole number of load passes");
+  constexpr int ROWB = D * 2;              // bytes per K/V row
+  constexpr int TILE_KV = BN * ROWB;       // one K or V tile, 16 KB
+  constexpr int STAGE_B = 2 * TILE_KV;     // K then V
+  constexpr int STAGES = 4;
   constexpr int NKB = BN / 32;             // 2
   constexpr int NDB = D / 32;              // 4
   constexpr int NDC = D / 16;              // 8
@@ -75,6 +102,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   constexpr int NPV = NKC * NDB;           // P~V MFMAs per tile
   constexpr int NQK = NDC * NKB;           // QK^T MFMAs per tile
   static_assert(NPV == NQK, "the fused matrix phase pairs one P~V and one QK^T MFMA");
+  static_assert(NT == 512 && D == 128 && BN == 64, "the loader gives each wave four 1 KB blocks");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE_B];
 
@@ -168,40 +196,41 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   }
   const int lim_h = lim - 4 * hh;
 
-  // ---- loader: buffer loads (keys past skv read as zero) into the ring
-  const int ld_c = tid % CH;
-  const int ld_r = tid / CH;
-  const int ld_voff = ld_r * ROWB + ld_c * 16;
-  const int st_k = ld_r * KSTR + ld_c * 16;
-  const int st_v = KTILE_B + ld_r * VSTR + ld_c * 16;
-  u32x4 kreg[PASSES], vreg[PASSES];
-  auto gload = [&](int u) {
+  // ---- HBM -> LDS in MFMA fragment order, no registers on the way (keys
+  // past skv arrive as zeros).  K block j = 8 kbi + c (1 KB): lane L holds
+  // K[32 kbi + L%32][16c + 8(L/32) ..+8].  V block j = 4 kc + db (1 KB) = two
+  // transposed-read blocks e = L/32 of 512 B: lane L holds
+  // V[16kc + 8e + 4(g>>1) + (L%8)/2][32db + 16(g&1) + 8(L%2) ..+8], g = (L%32)/8.
+  // Waves 0-3 load K blocks (32 keys, columns 64(w%2) ..+64), waves 4-7 the V
+  // blocks of 16 keys each: every wave reads whole 128-byte lines.
+  const int k_lane_g = l32 * ROWB + hh * 16;
+  const int vg = l32 >> 3;
+  const int v_lane_g = (8 * hh + 4 * (vg >> 1) + ((lane & 7) >> 1)) * ROWB + (16 * (vg & 1) + 8 * (lane & 1)) * 2;
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  auto load_tile = [&](int u) {
     const int k0 = u * BN;
     const int nrows = skv - k0 < BN ? skv - k0 : BN;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + (int64_t)k0 * D, nrows * ROWB);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + (int64_t)k0 * D, nrows * ROWB);
+    const unsigned st = lds_u32(smem) + (u % STAGES) * STAGE_B;
+    if (wu < 4) {
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(K + (int64_t)k0 * D, nrows * ROWB);
+      const int kbi = wu >> 1;
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-      kreg[i] = buffer_load16(kr, ld_voff, i * RPP * ROWB);
-      vreg[i] = buffer_load16(vr, ld_voff, i * RPP * ROWB);
-    }
-  };
-  auto lstore = [&](int u) {
-    unsigned char* sb = smem + (u % STAGES) * STAGE_B;
+      for (int i = 0; i < 4; ++i) {
+        const int c = 4 * (wu & 1) + i;
+        load_lds16(r, k_lane_g, kbi * 32 * ROWB + c * 32, st + (8 * kbi + c) * 1024);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(V + (int64_t)k0 * D, nrows * ROWB);
+      const int kc = wu - 4;
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-      *(u32x4*)(sb + st_k + i * RPP * KSTR) = kreg[i];
-      *(u32x4*)(sb + st_v + i * RPP * VSTR) = vreg[i];
+      for (int db = 0; db < 4; ++db) load_lds16(r, v_lane_g, kc * 16 * ROWB + db * 64, st + TILE_KV + (4 * kc + db) * 1024);
     }
   };
 
-  // per-lane LDS offsets: K operand row l32, chunk hh (+32kb rows, +2c
-  // chunks); transposed V read at row 4(g>>1) + (t>>2), column
-  // 16(g&1) + 4(t&3) of a 16-lane group (g, t) (+16kc + 8e rows, +32db)
-  const int g16 = lane >> 4;
-  const int t16 = lane & 15;
-  const int k_lane = l32 * KSTR + 16 * hh;
-  const int v_lane = KTILE_B + (4 * (g16 >> 1) + (t16 >> 2)) * VSTR + (16 * (g16 & 1) + 4 * (t16 & 3)) * 2;
+  // per-lane LDS read offsets: fragment blocks are read whole, lane L at 16L
+  // (K, ds_read_b128) or 8L (V, two ds_read_b64_tr_b16 per fragment)
+  const int k_lane = lane * 16;
+  const int v_lane = TILE_KV + lane * 8;
 
   // ---- state
   f32x16 oacc[NDB];
@@ -213,25 +242,20 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   f32x16 s[NKB];             // S^T of the current tile
   bf16x8 pb[NKC];            // P~ of the tile waiting for its P~V product
 
-  // ---- prologue: tiles 0..2 into the ring
-#pragma unroll
-  for (int u = 0; u < STAGES; ++u) {
-    if (u < nt) {
-      gload(u);
-      lstore(u);
-    }
-  }
+  // ---- prologue: tiles 0 and 1
+  for (int u = 0; u < 2; ++u)
+    if (u < nt) load_tile(u);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   const int nslots = 2 * nt + 2;
   for (int slot = 0; slot < nslots; ++slot) {
-    // HBM -> registers two slots ahead, registers -> LDS after the stage's
-    // previous tile has been read for the last time
+    // slot 2k fetches tile k+2 into the stage of tile k-2, whose last read
+    // (its V, by group B) was in slot 2k-1; tile k+2 is first read in slot
+    // 2k+4
     if ((slot & 1) == 0) {
       const int k = slot >> 1;
-      if (k >= 2 && k + 1 < nt) lstore(k + 1);
-      if (k >= 1 && k + 2 < nt) gload(k + 2);
+      if (k + 2 < nt) load_tile(k + 2);
     }
 
     const int ls = slot - grp;  // this group's own slot index
@@ -248,12 +272,12 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
         __builtin_amdgcn_s_setprio(ATTN_PP_PRIO);
         const unsigned char* vb = smem + ((t + STAGES - 1) % STAGES) * STAGE_B + v_lane;
         const unsigned char* kb = smem + (t % STAGES) * STAGE_B + k_lane;
+        // fragment (c, kbi) of K and (kc, db) of V, block offsets as immediates
         auto vfrag = [&](int kc, int db) {
-          const s16x4 lo = lds_read_tr16(vb + 16 * kc * VSTR + 64 * db);
-          const s16x4 hi = lds_read_tr16(vb + (16 * kc + 8) * VSTR + 64 * db);
-          return join_tr(lo, hi);
+          const unsigned char* a = vb + (4 * kc + db) * 1024;
+          return join_tr(lds_read_tr16(a), lds_read_tr16(a + 512));
         };
-        auto kfrag = [&](int c, int kbi) { return *(const bf16x8*)(kb + kbi * 32 * KSTR + 32 * c); };
+        auto kfrag = [&](int c, int kbi) { return *(const bf16x8*)(kb + (8 * kbi + c) * 1024); };
         if (do_pv && do_qk) {
           // steady state: the 16 P~V and 16 QK^T MFMAs are independent, so
           // they are issued alternately, each with its operand read a few
@@ -268,15 +292,15 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
             const int c = i / NKB, kbi = i % NKB;
             s[kbi] = mfma32(kfrag(c, kbi), qf[c], s[kbi]);
           }
-          __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 3 * ATTN_PP_AHEAD, 0);
 #pragma unroll
-          for (int i = 0; i < NPV - 2; ++i) {
+          for (int i = 0; i < NPV - ATTN_PP_AHEAD; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * ATTN_PP_AHEAD, 0);
         } else {
         bf16x8 kf[2][NKB];
         if (do_pv) {
@@ -325,17 +349,36 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
             for (int r = 0; r < 16; ++r)  // key = k0 + 32kbi + 8(r/4) + 4hh + r%4
               if (k0 + 32 * kbi + 8 * (r >> 2) + (r & 3) >= lim_h) s[kbi][r] = -INFINITY;
         }
-        // row max and row sum as four independent partial chains
-        float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        // P~ against the current reference, S kept; this lane's share of the
+        // row sum as four independent chains
+        auto expo = [&]() {
+          float rp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kbi = 0; kbi < NKB; ++kbi)
+          for (int kc = 0; kc < NKC; ++kc) {
+            const f32x16& sk = s[kc >> 1];
+            const int rb = 8 * (kc & 1);
+            float e[8];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[kbi][r]);
-        float mx = pair32_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
-        const bool need = (mx > m_used) && ((mx - m_used) * sl2 > kTau);
-        if (__any(need)) {
-          const float m_new = need ? mx : m_used;
-          const float alpha = need ? fast_exp2((m_used - m_new) * sl2) : 1.0f;
+            for (int j = 0; j < 8; ++j) {
+              e[j] = fast_exp2(fmaf(sk[rb + j], sl2, neg_ms));
+              rp[j & 3] += e[j];
+            }
+            pb[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+          }
+          return (rp[0] + rp[1]) + (rp[2] + rp[3]);
+        };
+        float ps = expo();
+        // a share above 2^8 means some P~ above 2^8, and a row without a
+        // reference has no P~ yet: exact reference update, then P~ again
+        if (__any(ps > kSumCap || m_used == -INFINITY)) {
+          float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+          for (int kbi = 0; kbi < NKB; ++kbi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[kbi][r]);
+          const float mx = pair32_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+          const float m_new = fmaxf(m_used, mx);
+          const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2((m_used - m_new) * sl2);
           l_part *= alpha;
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
@@ -343,24 +386,19 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
             for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
           m_used = m_new;
           neg_ms = (m_used == -INFINITY) ? 0.0f : -m_used * sl2;
+          ps = expo();
         }
-        float rp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kbi = 0; kbi < NKB; ++kbi)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = fast_exp2(fmaf(s[kbi][r], sl2, neg_ms));
-            s[kbi][r] = e;
-            rp[r & 3] += e;
-          }
-        l_part += (rp[0] + rp[1]) + (rp[2] + rp[3]);
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          const f32x16& sk = s[kc >> 1];
-          const int rb = 8 * (kc & 1);
-          pb[kc] = to_bf16x8(sk[rb + 0], sk[rb + 1], sk[rb + 2], sk[rb + 3], sk[rb + 4], sk[rb + 5],
-                             sk[rb + 6], sk[rb + 7]);
-        }
+        l_part += ps;
+      }
+    }
+    if (slot & 1) {
+      // tile k+1 must have landed before slot 2k+2 reads it; tile k+2's
+      // four loads may still be in flight (s_waitcnt immediate: expcnt and
+      // lgkmcnt at their maxima, vmcnt in the low four bits)
+      if ((slot >> 1) + 2 < nt) {
+        __builtin_amdgcn_s_waitcnt(0x0F74);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
       }
     }
     __syncthreads();
