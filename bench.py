@@ -108,7 +108,7 @@ def run_workload(name: str, steps: int, warmup: int, inputs=None):
     return wl, ns, t
 
 
-def cpu_baseline(name: str, inputs, target_s: float = 12.0):
+def cpu_baseline(name: str, inputs, target_s: float = 15.0):
     """The oracle as it stands, on a bounded sample of query rows of the
     same workload (every key of each sampled row), on the host cores."""
     import numpy as np
@@ -123,10 +123,11 @@ def cpu_baseline(name: str, inputs, target_s: float = 12.0):
         idx = np.arange(n, dtype=np.int64) * 7919 % (wl.B * wl.H * wl.Sq)
         return np.stack([idx // (wl.H * wl.Sq), (idx // wl.Sq) % wl.H, idx % wl.Sq], axis=1)
 
+    n_cal = 4096
     t0 = time.perf_counter()
-    oracle.attention(q, k, v, wl.scale, wl.causal, rows=rows_for(512), nthreads=threads)
+    oracle.attention(q, k, v, wl.scale, wl.causal, rows=rows_for(n_cal), nthreads=threads)
     cal = time.perf_counter() - t0
-    n = int(min(wl.B * wl.H * wl.Sq, max(512, 512 * target_s / max(cal, 1e-3))))
+    n = int(min(wl.B * wl.H * wl.Sq, max(n_cal, n_cal * target_s / max(cal, 1e-3))))
     rows = rows_for(n)
     t0 = time.perf_counter()
     oracle.attention(q, k, v, wl.scale, wl.causal, rows=rows, nthreads=threads)

@@ -4,8 +4,8 @@
 // decode row left O_s (normalised by its own l_s) and glse_s = log2 l_s +
 // m_s * s * log2(e).  The output is sum_s w_s O_s with w_s = l_s / sum l,
 // computed as 2^(glse_s - glse_tot), glse_tot = log2 sum 2^(glse_s - max) +
-// max.  The splits are visited in index order by one lane each, so the
-// result is bitwise reproducible.  Empty splits carry glse = -inf and weigh
+// max.  Every reduction has a fixed order, so the result is bitwise
+// reproducible.  Empty splits carry glse = -inf and weigh
 // nothing; a row with no key at all gets O = 0 and LSE = -inf.
 #include "attn_common.h"
 #include "attn_internal.h"
@@ -23,39 +23,58 @@ __device__ inline float cast_out<float>(float x) { return x; }
 template <>
 __device__ inline __bf16 cast_out<__bf16>(float x) { return (__bf16)x; }
 
-// one wave per (b, h) row; each lane owns D/64 columns
+// one wave per (b, h) row.  The split LSEs are spread over the lanes (lane
+// s % 64 holds split s) and reduced with a fixed butterfly; the partial rows
+// are then read sixteen splits at a time, all loads in flight together, and
+// added in split order.  Each lane owns D/64 adjacent columns.
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void combine_kernel(const Params p) {
   constexpr int DPL = D / 64;
+  constexpr int CHUNK = 16;
+  typedef float vec_t __attribute__((ext_vector_type(DPL)));
   const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long row = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= (long)p.B * p.H) return;
   const int S = p.num_splits;
   const float* gl = p.ws_lse + row * S;
-  const float* po = p.ws_o + row * S * D;
+  const float* po = p.ws_o + row * S * D + lane * DPL;
 
   float gmax = -INFINITY;
-  for (int s = 0; s < S; ++s) gmax = fmaxf(gmax, gl[s]);
-  OutT* orow = (OutT*)p.o + row * D;
+  for (int s0 = 0; s0 < S; s0 += 64)
+    if (s0 + lane < S) gmax = fmaxf(gmax, gl[s0 + lane]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) gmax = fmaxf(gmax, shfl_xor_f(gmax, m));
+  OutT* orow = (OutT*)p.o + row * D + lane * DPL;
   if (gmax == -INFINITY) {
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) orow[lane * DPL + j] = cast_out<OutT>(0.0f);
+    for (int j = 0; j < DPL; ++j) orow[j] = cast_out<OutT>(0.0f);
     if (p.lse != nullptr && lane == 0) p.lse[row] = -INFINITY;
     return;
   }
   float tot = 0.0f;
-  for (int s = 0; s < S; ++s) tot += fast_exp2(gl[s] - gmax);
+  for (int s0 = 0; s0 < S; s0 += 64)
+    if (s0 + lane < S) tot += fast_exp2(gl[s0 + lane] - gmax);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) tot += shfl_xor_f(tot, m);
   const float gtot = fast_log2(tot) + gmax;
-  float acc[DPL];
+
+  vec_t acc = {};
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    // weight of split s0 + lane in this lane, handed out with readlane
+    const float wl = s0 + lane < S ? fast_exp2(gl[s0 + lane] - gtot) : 0.0f;
+    const int n = S - s0 < 64 ? S - s0 : 64;
+    for (int c0 = 0; c0 < n; c0 += CHUNK) {
+      vec_t part[CHUNK];
 #pragma unroll
-  for (int j = 0; j < DPL; ++j) acc[j] = 0.0f;
-  for (int s = 0; s < S; ++s) {
-    const float w = fast_exp2(gl[s] - gtot);
+      for (int j = 0; j < CHUNK; ++j)
+        part[j] = c0 + j < n ? *(const vec_t*)(po + (long)(s0 + c0 + j) * D) : vec_t{};
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) acc[j] = fmaf(w, po[(long)s * D + lane * DPL + j], acc[j]);
+      for (int j = 0; j < CHUNK; ++j)
+        acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), c0 + j)) * part[j];
+    }
   }
 #pragma unroll
-  for (int j = 0; j < DPL; ++j) orow[lane * DPL + j] = cast_out<OutT>(acc[j]);
+  for (int j = 0; j < DPL; ++j) orow[j] = cast_out<OutT>(acc[j]);
   if (p.lse != nullptr && lane == 0) p.lse[row] = gtot * kLn2;
 }
 
