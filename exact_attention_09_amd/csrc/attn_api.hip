@@ -1,6 +1,7 @@
 // C-ABI entry points: argument validation (before any HIP call), path
 // selection (tiled forward, split-KV decode, no-key fill) and the split
 // workspace.  See include/attn.h for the contract.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -57,6 +58,19 @@ int heuristic_splits(int B, int Hkv, int Skv) {
 }
 
 }  // namespace
+
+// compute units of the current device, looked up once per device
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 extern "C" {
 
@@ -143,6 +157,15 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
     if (work > 0x7ffffff0L) return fail(ATTN_EINVAL, "too many query tiles");
     p.tiles_per_head = (int)tiles;
     p.work_items = (int)work;
+    // a persistent grid of one workgroup per CU when the work items divide
+    // evenly over the CUs (the kernel pairs heavy and light causal tiles);
+    // otherwise one workgroup per item and the hardware dispatcher balances
+    p.persist_c = 0;
+    if (pingpong && !varlen && getenv("ATTN_NO_PERSIST") == nullptr) {
+      const int cus = device_cus();
+      const long c = cus / 8;
+      if (c > 0 && cus % 8 == 0 && work % (8 * c) == 0) p.persist_c = (int)c;
+    }
     const hipError_t e = !bf16 ? attn::launch_f32(p, false, st)
                                : (pingpong ? attn::launch_prefill_pp(p, st) : attn::launch_prefill_bf16(p, st));
     return e == hipSuccess ? ATTN_OK : hip_fail(e, "forward kernel");

@@ -29,6 +29,7 @@ struct Params {
   int split_len;           // keys per split: ceil(Skv / num_splits)
   int tiles_per_head;      // query tiles per (b, h) (varlen: upper bound per head)
   int work_items;          // real work items; the grid may be padded to 8k
+  int persist_c;           // > 0: persistent grid of 8 x persist_c workgroups (see the kernel)
 };
 
 // ---------------------------------------------------------------- helpers

@@ -20,13 +20,13 @@
 //     runs one slot behind group A, so the roles alternate every slot.
 //   * Each wave keeps a single S tile in registers (32 rows x 64 keys), so the
 //     register footprint is that of the plain loop (2 waves per SIMD).
-//   * K/V tiles (64 keys) live in a four-stage LDS ring (128 KB).  A tile
-//     is read during four consecutive slots (K by A then B, V by A then B
-//     two slots later).  Tiles go from HBM straight to LDS (buffer_load ...
+//   * K/V tiles (64 keys) live in a ring of PF + 2 LDS stages of 32 KB.  A
+//     tile is read during four consecutive slots (K by A then B, V by A then
+//     B two slots later).  Tiles go from HBM straight to LDS (buffer_load ...
 //     lds, no registers on the way), laid out in MFMA fragment order; tile u
-//     is fetched in slot 2u-4 into the stage of tile u-4, after the barrier
-//     that ends that tile's last read, and waited for at the end of slot
-//     2u-1.
+//     is fetched in slot 2(u-PF) into the stage of tile u-PF-2, after the
+//     barrier that ends that tile's last read, and waited for at the end of
+//     slot 2u-1.
 //   * S^T = K Q^T and O^T = V^T P~^T on v_mfma_f32_32x32x16_bf16 (one query
 //     row per lane), K read with ds_read_b128, V with ds_read_b64_tr_b16.
 //     Each fragment read covers one contiguous block (1 KB or 512 B), so it
@@ -57,6 +57,9 @@ constexpr float kLn2 = 0.69314718055994530942f;
 #endif
 #ifndef ATTN_PP_PRIO
 #define ATTN_PP_PRIO 2
+#endif
+#ifndef ATTN_PP_PF
+#define ATTN_PP_PF 2
 #endif
 #ifndef ATTN_PP_AHEAD
 #define ATTN_PP_AHEAD 3
@@ -94,7 +97,8 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   constexpr int ROWB = D * 2;              // bytes per K/V row
   constexpr int TILE_KV = BN * ROWB;       // one K or V tile, 16 KB
   constexpr int STAGE_B = 2 * TILE_KV;     // K then V
-  constexpr int STAGES = 4;
+  constexpr int PF = ATTN_PP_PF;           // tiles fetched ahead
+  constexpr int STAGES = PF + 2;
   constexpr int NKB = BN / 32;             // 2
   constexpr int NDB = D / 32;              // 4
   constexpr int NDC = D / 16;              // 8
@@ -114,9 +118,8 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   const int hh = lane >> 5;
   const float sl2 = p.scale_log2;
 
-  // ---- work item -> (b, h, query tile)
-  const int v = xcd_remap(blockIdx.x, p.work_items);
-  if (v < 0) return;
+  // ---- one work item v: (b, h, query tile)
+  auto run_item = [&](const int v) {
   int h, tile, sq, skv, off;
   int64_t q_row0, kv_row0;
   if constexpr (!VARLEN) {
@@ -164,7 +167,9 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   __bf16* __restrict__ O = (__bf16*)p.o + q_row0 * D;
 
   const int q0 = tile * BM;
-  const int qw0 = q0 + 128 * grp + 32 * (wave & 3);
+  // the two waves on a SIMD take the two 32-row halves of one 64-row block,
+  // so under a causal mask they end on the same key tile
+  const int qw0 = q0 + 64 * (wave & 3) + 32 * grp;
   const int qrow = qw0 + l32;
 
   // ---- Q fragments (B operand of S^T = K Q^T): row qrow, d = 16c + 8hh + j
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   bf16x8 pb[NKC];            // P~ of the tile waiting for its P~V product
 
   // ---- prologue: tiles 0 and 1
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < PF; ++u)
     if (u < nt) load_tile(u);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     // 2k+4
     if ((slot & 1) == 0) {
       const int k = slot >> 1;
-      if (k + 2 < nt) load_tile(k + 2);
+      if (k + PF < nt) load_tile(k + PF);
     }
 
     const int ls = slot - grp;  // this group's own slot index
@@ -392,10 +397,15 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
       }
     }
     if (slot & 1) {
-      // tile k+1 must have landed before slot 2k+2 reads it; tile k+2's
-      // four loads may still be in flight (s_waitcnt immediate: expcnt and
-      // lgkmcnt at their maxima, vmcnt in the low four bits)
-      if ((slot >> 1) + 2 < nt) {
+      // tile k+1 must have landed before slot 2k+2 reads it; the four loads
+      // of each of tiles k+2 .. k+PF may still be in flight (s_waitcnt
+      // immediate: expcnt and lgkmcnt at their maxima, vmcnt in the low four
+      // bits)
+      const int k = slot >> 1;
+      const int newer = (nt - 1 < k + PF ? nt - 1 : k + PF) - (k + 1);
+      if (PF >= 3 && newer >= 2) {
+        __builtin_amdgcn_s_waitcnt(0x0F78);
+      } else if (newer >= 1) {
         __builtin_amdgcn_s_waitcnt(0x0F74);
       } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -423,11 +433,31 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     if (p.lse != nullptr && hh == 0)
       p.lse[q_row0 + qrow] = l > 0.0f ? (m_used * sl2 + fast_log2(l)) * kLn2 : -INFINITY;
   }
+  };
+
+  if (p.persist_c == 0) {
+    // one workgroup per work item, in XCD-aware order
+    const int v = xcd_remap(blockIdx.x, p.work_items);
+    if (v >= 0) run_item(v);
+  } else {
+    // persistent grid: one workgroup per CU (8 XCDs x persist_c CUs; the
+    // work-item count is a multiple of that).  Workgroup g sits on XCD g % 8
+    // and walks that XCD's share of the items in rounds of persist_c,
+    // reversing direction every round, so that a heavy causal tile (items of
+    // a head run heavy first) is paired with a light one.
+    const int C = p.persist_c;
+    const int x = blockIdx.x % 8, c = blockIdx.x / 8;
+    const int per = p.work_items / 8;
+    for (int r = 0; r * C < per; ++r) {
+      run_item(x * per + r * C + ((r & 1) ? C - 1 - c : c));
+      __syncthreads();
+    }
+  }
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_one(const Params& p, hipStream_t st) {
-  const int grid = 8 * ceil_div(p.work_items, 8);
+  const int grid = p.persist_c > 0 ? 8 * p.persist_c : 8 * ceil_div(p.work_items, 8);
   hipLaunchKernelGGL((prefill_pp_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(512), 0, st, p);
   return hipGetLastError();
 }
