@@ -147,9 +147,8 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
 
   const bool decode = !varlen && Sq == 1;
   if (!decode) {
-    // d = 64 stays on the basic kernel: its 4-wave workgroups fit several per
-    // CU, and at half the MFMA work per tile the vector work sets the pace
-    const bool pingpong = bf16 && d == 128 && getenv("ATTN_BASIC_PREFILL") == nullptr;
+    // ATTN_BASIC_PREFILL selects the basic tiled kernel instead
+    const bool pingpong = bf16 && getenv("ATTN_BASIC_PREFILL") == nullptr;
     const int bm = !bf16 ? attn::f32_block_m()
                          : (pingpong ? attn::prefill_pp_block_m() : attn::prefill_bf16_block_m());
     const long tiles = varlen ? (long)Sq / bm + B : attn::ceil_div(Sq, bm);

@@ -11,7 +11,7 @@ namespace attn {
 int prefill_bf16_block_m();
 hipError_t launch_prefill_bf16(const Params& p, hipStream_t st);
 
-// bf16 tiled forward, two wave groups in ping-pong (BM = 256), d = 128.
+// bf16 tiled forward, two wave groups in ping-pong (BM = 256), d = 64 or 128.
 int prefill_pp_block_m();
 hipError_t launch_prefill_pp(const Params& p, hipStream_t st);
 

@@ -1,4 +1,4 @@
-// Tiled forward for bf16 (d = 128), with matrix and vector phases of two wave
+// Tiled forward for bf16 (d = 64 or 128), with matrix and vector phases of two wave
 // groups interleaved ("ping-pong"), gfx950.
 //
 // Same method as the basic tiled kernel (TileLang tutorial chapter 15,
@@ -52,9 +52,6 @@ namespace {
 constexpr float kSumCap = 256.0f;  // 2^8: bound on a lane's share of a tile row sum
 constexpr float kLn2 = 0.69314718055994530942f;
 
-#ifndef ATTN_PP_BN
-#define ATTN_PP_BN 64
-#endif
 #ifndef ATTN_PP_PRIO
 #define ATTN_PP_PRIO 2
 #endif
@@ -90,7 +87,7 @@ __device__ inline unsigned lds_u32(const void* p) {
 
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
-  constexpr int BN = ATTN_PP_BN;
+  constexpr int BN = D == 128 ? 64 : 128;  // keys per tile: 16 + 16 MFMAs per matrix phase
   constexpr int NW = 8;
   constexpr int BM = 32 * NW;              // 256
   constexpr int NT = 64 * NW;              // 512 threads
@@ -99,14 +96,14 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   constexpr int STAGE_B = 2 * TILE_KV;     // K then V
   constexpr int PF = ATTN_PP_PF;           // tiles fetched ahead
   constexpr int STAGES = PF + 2;
-  constexpr int NKB = BN / 32;             // 2
-  constexpr int NDB = D / 32;              // 4
-  constexpr int NDC = D / 16;              // 8
-  constexpr int NKC = BN / 16;             // 4
+  constexpr int NKB = BN / 32;             // 32-key blocks of a tile
+  constexpr int NDB = D / 32;              // 32-column blocks of d
+  constexpr int NDC = D / 16;              // 16-column chunks of d
+  constexpr int NKC = BN / 16;             // 16-key chunks of a tile
   constexpr int NPV = NKC * NDB;           // P~V MFMAs per tile
   constexpr int NQK = NDC * NKB;           // QK^T MFMAs per tile
   static_assert(NPV == NQK, "the fused matrix phase pairs one P~V and one QK^T MFMA");
-  static_assert(NT == 512 && D == 128 && BN == 64, "the loader gives each wave four 1 KB blocks");
+  static_assert(NT == 512 && NDC * NKB == 16 && NKC * NDB == 16, "the loader gives each wave four 1 KB blocks");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE_B];
 
@@ -202,12 +199,12 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   const int lim_h = lim - 4 * hh;
 
   // ---- HBM -> LDS in MFMA fragment order, no registers on the way (keys
-  // past skv arrive as zeros).  K block j = 8 kbi + c (1 KB): lane L holds
-  // K[32 kbi + L%32][16c + 8(L/32) ..+8].  V block j = 4 kc + db (1 KB) = two
-  // transposed-read blocks e = L/32 of 512 B: lane L holds
+  // past skv arrive as zeros).  K block j = (d/16) kbi + c (1 KB): lane L
+  // holds K[32 kbi + L%32][16c + 8(L/32) ..+8].  V block j = (d/32) kc + db
+  // (1 KB) = two transposed-read blocks e = L/32 of 512 B: lane L holds
   // V[16kc + 8e + 4(g>>1) + (L%8)/2][32db + 16(g&1) + 8(L%2) ..+8], g = (L%32)/8.
-  // Waves 0-3 load K blocks (32 keys, columns 64(w%2) ..+64), waves 4-7 the V
-  // blocks of 16 keys each: every wave reads whole 128-byte lines.
+  // Waves 0-3 load the K blocks 4w .. 4w+3, waves 4-7 the V blocks
+  // 4(w-4) .. +3: every wave reads whole 128-byte lines.
   const int k_lane_g = l32 * ROWB + hh * 16;
   const int vg = l32 >> 3;
   const int v_lane_g = (8 * hh + 4 * (vg >> 1) + ((lane & 7) >> 1)) * ROWB + (16 * (vg & 1) + 8 * (lane & 1)) * 2;
@@ -218,17 +215,18 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     const unsigned st = lds_u32(smem) + (u % STAGES) * STAGE_B;
     if (wu < 4) {
       const __amdgpu_buffer_rsrc_t r = make_rsrc(K + (int64_t)k0 * D, nrows * ROWB);
-      const int kbi = wu >> 1;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = 4 * (wu & 1) + i;
-        load_lds16(r, k_lane_g, kbi * 32 * ROWB + c * 32, st + (8 * kbi + c) * 1024);
+        const int j = 4 * wu + i, kbi = j / NDC, c = j % NDC;
+        load_lds16(r, k_lane_g, kbi * 32 * ROWB + c * 32, st + j * 1024);
       }
     } else {
       const __amdgpu_buffer_rsrc_t r = make_rsrc(V + (int64_t)k0 * D, nrows * ROWB);
-      const int kc = wu - 4;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) load_lds16(r, v_lane_g, kc * 16 * ROWB + db * 64, st + TILE_KV + (4 * kc + db) * 1024);
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * (wu - 4) + i, kc = j / NDB, db = j % NDB;
+        load_lds16(r, v_lane_g, kc * 16 * ROWB + db * 64, st + TILE_KV + j * 1024);
+      }
     }
   };
 
@@ -279,10 +277,10 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
         const unsigned char* kb = smem + (t % STAGES) * STAGE_B + k_lane;
         // fragment (c, kbi) of K and (kc, db) of V, block offsets as immediates
         auto vfrag = [&](int kc, int db) {
-          const unsigned char* a = vb + (4 * kc + db) * 1024;
+          const unsigned char* a = vb + (NDB * kc + db) * 1024;
           return join_tr(lds_read_tr16(a), lds_read_tr16(a + 512));
         };
-        auto kfrag = [&](int c, int kbi) { return *(const bf16x8*)(kb + (8 * kbi + c) * 1024); };
+        auto kfrag = [&](int c, int kbi) { return *(const bf16x8*)(kb + (NDC * kbi + c) * 1024); };
         if (do_pv && do_qk) {
           // steady state: the 16 P~V and 16 QK^T MFMAs are independent, so
           // they are issued alternately, each with its operand read a few
@@ -475,8 +473,9 @@ int prefill_pp_block_m() { return 256; }
 
 hipError_t launch_prefill_pp(const Params& p, hipStream_t st) {
   if (p.work_items <= 0) return hipSuccess;
-  if (p.d != 128) return hipErrorInvalidValue;
-  return launch_d<128>(p, st);
+  if (p.d == 128) return launch_d<128>(p, st);
+  if (p.d == 64) return launch_d<64>(p, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace attn

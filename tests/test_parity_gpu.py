@@ -256,24 +256,28 @@ def test_varlen_edges(case):
     check(o[0], lse[0], o_ref, lse_ref, dtype, str(case))
 
 
-BASIC_D128 = [
-    ("dense", 1, 2, 2, 257, 257, True),
-    ("dense", 2, 4, 1, 77, 200, True),
-    ("dense", 1, 2, 2, 300, 130, False),
-    ("varlen", (5, 0, 127, 128, 300), 4, 2, 0, 0, True),
+BASIC = [
+    ("dense", 1, 2, 2, 257, 257, True, 128),
+    ("dense", 2, 4, 1, 77, 200, True, 128),
+    ("dense", 1, 2, 2, 300, 130, False, 128),
+    ("dense", 2, 6, 3, 200, 200, True, 64),
+    ("dense", 1, 2, 2, 300, 130, True, 64),
+    ("varlen", (5, 0, 127, 128, 300), 4, 2, 0, 0, True, 128),
+    ("varlen", (5, 0, 127, 128, 300), 4, 4, 0, 0, False, 64),
 ]
 
 
-@pytest.mark.parametrize("case", BASIC_D128, ids=lambda c: "-".join(map(str, c)))
-def test_basic_kernel_d128(case, monkeypatch):
-    """d = 128 prefill normally runs the ping-pong kernel; ATTN_BASIC_PREFILL
+@pytest.mark.parametrize("case", BASIC, ids=lambda c: "-".join(map(str, c)))
+def test_basic_kernel(case, monkeypatch):
+    """bf16 prefill normally runs the ping-pong kernel; ATTN_BASIC_PREFILL
     selects the basic tiled kernel, which must meet the same bar."""
     monkeypatch.setenv("ATTN_BASIC_PREFILL", "1")
-    say(f"basic d128 case {case}")
+    say(f"basic kernel case {case}")
     seed = zlib.crc32(repr(case).encode()) % 10000
-    d, scale = 128, 1.0 / math.sqrt(128)
+    d = case[-1]
+    scale = 1.0 / math.sqrt(d)
     if case[0] == "varlen":
-        _, lengths, H, Hkv, _, _, causal = case
+        _, lengths, H, Hkv, _, _, causal, _ = case
         T = sum(lengths)
         cu = synth.cu_seqlens_from_lengths(lengths)
         q, k, v = (synth.normal_tensor(seed * 10 + i, (1, h, T, d), "bf16") for i, h in enumerate((H, Hkv, Hkv)))
@@ -282,13 +286,29 @@ def test_basic_kernel_d128(case, monkeypatch):
                                           host_f32(v, "bf16")[0], scale, causal, cu_seqlens=cu)
         check(o[0], lse[0], o_ref, lse_ref, "bf16", str(case))
         return
-    _, B, H, Hkv, Sq, Skv, causal = case
+    _, B, H, Hkv, Sq, Skv, causal, _ = case
     q = synth.normal_tensor(seed * 10 + 0, (B, H, Sq, d), "bf16")
     k = synth.normal_tensor(seed * 10 + 1, (B, Hkv, Skv, d), "bf16")
     v = synth.normal_tensor(seed * 10 + 2, (B, Hkv, Skv, d), "bf16")
     o, lse = gpu_run(q, k, v, "bf16", causal, scale)
     o_ref, lse_ref = oracle_dense(q, k, v, "bf16", scale, causal)
     check(o, lse, o_ref, lse_ref, "bf16", str(case))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dispatched_grid_matches_persistent(causal, monkeypatch):
+    """The d = 128 kernel runs a persistent grid when the query tiles divide
+    evenly over the CUs; the one-workgroup-per-tile grid (ATTN_NO_PERSIST)
+    must give bitwise the same result."""
+    import exact_attention_09_amd as ea
+    say(f"persistent vs dispatched, causal={causal}")
+    B, H, S, d = 1, 32, 2048, 128
+    q, k, v = (to_device(synth.normal_tensor(9100 + i, (B, H, S, d), "bf16"), "bf16") for i in range(3))
+    o1, l1 = ea.attn_fwd(q, k, v, causal=causal)
+    monkeypatch.setenv("ATTN_NO_PERSIST", "1")
+    o2, l2 = ea.attn_fwd(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 # ------------------------------------------------------------ determinism, canaries
