@@ -140,8 +140,8 @@ def cpu_baseline(name: str, inputs, target_s: float = 15.0):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--quick", action="store_true", help="headline workload only, no CPU baseline")
     ap.add_argument("--workload", default=HEADLINE, help="time only this workload (profiling runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
