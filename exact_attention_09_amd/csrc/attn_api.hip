@@ -156,14 +156,18 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
     if (work > 0x7ffffff0L) return fail(ATTN_EINVAL, "too many query tiles");
     p.tiles_per_head = (int)tiles;
     p.work_items = (int)work;
-    // a persistent grid of one workgroup per CU when the work items divide
-    // evenly over the CUs (the kernel pairs heavy and light causal tiles);
-    // otherwise one workgroup per item and the hardware dispatcher balances
+    // a persistent grid of one workgroup per CU (the kernel pairs heavy and
+    // light causal tiles): dense when the items divide evenly over the CUs,
+    // varlen when locating an item (a scan over sequences and tile indices)
+    // stays short; otherwise one workgroup per item and the hardware
+    // dispatcher balances.  ATTN_NO_PERSIST forces the latter.
     p.persist_c = 0;
-    if (pingpong && !varlen && getenv("ATTN_NO_PERSIST") == nullptr) {
+    if (pingpong && getenv("ATTN_NO_PERSIST") == nullptr) {
       const int cus = device_cus();
       const long c = cus / 8;
-      if (c > 0 && cus % 8 == 0 && work % (8 * c) == 0) p.persist_c = (int)c;
+      const bool fits = varlen ? H % 8 == 0 && B <= 1024 && (long)B * attn::ceil_div(Sq, bm) <= 1L << 16
+                               : work % (8 * c > 0 ? 8 * c : 1) == 0;
+      if (c > 0 && cus % 8 == 0 && fits) p.persist_c = (int)c;
     }
     const hipError_t e = !bf16 ? attn::launch_f32(p, false, st)
                                : (pingpong ? attn::launch_prefill_pp(p, st) : attn::launch_prefill_bf16(p, st));

@@ -51,6 +51,8 @@ namespace {
 
 constexpr float kSumCap = 256.0f;  // 2^8: bound on a lane's share of a tile row sum
 constexpr float kLn2 = 0.69314718055994530942f;
+// sequences a varlen call may have for the persistent (listed) order
+constexpr int kMaxListedSeqs = 1024;
 
 #ifndef ATTN_PP_PRIO
 #define ATTN_PP_PRIO 2
@@ -81,6 +83,20 @@ __device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, int voff, int soff, 
 }
 #pragma clang diagnostic pop
 
+__device__ inline int64_t uniform64(int64_t x) {
+  const uint64_t u = (uint64_t)x;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// buffer descriptor of a wave-uniform base and size, kept in scalar registers
+// (the loads above take it as a scalar operand)
+__device__ inline __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const int64_t b = uniform64((int64_t)(uintptr_t)base);
+  return make_rsrc((const void*)(uintptr_t)b, __builtin_amdgcn_readfirstlane(bytes));
+}
+
 __device__ inline unsigned lds_u32(const void* p) {
   return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -106,6 +122,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   static_assert(NT == 512 && NDC * NKB == 16 && NKC * NDB == 16, "the loader gives each wave four 1 KB blocks");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE_B];
+  __shared__ int seq_tiles[kMaxListedSeqs];  // varlen persistent order: query tiles per sequence
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -115,49 +132,19 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   const int hh = lane >> 5;
   const float sl2 = p.scale_log2;
 
-  // ---- one work item v: (b, h, query tile)
-  auto run_item = [&](const int v) {
-  int h, tile, sq, skv, off;
-  int64_t q_row0, kv_row0;
-  if constexpr (!VARLEN) {
-    const int bh = v / p.tiles_per_head;
-    const int rank = v - bh * p.tiles_per_head;
-    tile = CAUSAL ? p.tiles_per_head - 1 - rank : rank;
-    const int b = bh / p.H;
-    h = bh - b * p.H;
-    sq = p.Sq;
-    skv = p.Skv;
-    off = skv - sq;
-    q_row0 = (int64_t)bh * sq;
-    kv_row0 = ((int64_t)b * p.Hkv + h / p.group) * skv;
-  } else {
-    h = v / p.tiles_per_head;
-    int vt = v - h * p.tiles_per_head;
-    if (CAUSAL) vt = p.tiles_per_head - 1 - vt;
-    const int T = p.Sq;
-    int acc = 0, start = 0;
-    tile = -1;
-    sq = 0;
-    for (int bb = 0; bb < p.B; ++bb) {
-      int s0 = p.cu[bb], s1 = p.cu[bb + 1];
-      s0 = s0 < 0 ? 0 : (s0 > T ? T : s0);
-      s1 = s1 < s0 ? s0 : (s1 > T ? T : s1);
-      const int nt = ceil_div(s1 - s0, BM);
-      if (vt < acc + nt) {
-        tile = vt - acc;
-        sq = s1 - s0;
-        start = s0;
-        break;
-      }
-      acc += nt;
-    }
-    if (tile < 0) return;
-    skv = sq;
-    off = 0;
-    q_row0 = (int64_t)h * T + start;
-    kv_row0 = (int64_t)(h / p.group) * T + start;
-  }
-
+  // ---- one work item: query tile `tile` of a sequence of sq query rows
+  // and skv keys (causal offset off) whose rows start at q_row0 (queries)
+  // and kv_row0 (keys) in the head-major layout
+  auto work = [&](const int tile_a, const int sq_a, const int skv_a, const int off_a, const int64_t q_row0_a,
+                  const int64_t kv_row0_a) {
+  // the arguments are wave-uniform; readfirstlane lets the compiler keep them
+  // (and the load descriptors built from them) in scalar registers
+  const int tile = __builtin_amdgcn_readfirstlane(tile_a);
+  const int sq = __builtin_amdgcn_readfirstlane(sq_a);
+  const int skv = __builtin_amdgcn_readfirstlane(skv_a);
+  const int off = __builtin_amdgcn_readfirstlane(off_a);
+  const int64_t q_row0 = uniform64(q_row0_a);
+  const int64_t kv_row0 = uniform64(kv_row0_a);
   const __bf16* __restrict__ Q = (const __bf16*)p.q + q_row0 * D;
   const __bf16* __restrict__ K = (const __bf16*)p.k + kv_row0 * D;
   const __bf16* __restrict__ V = (const __bf16*)p.v + kv_row0 * D;
@@ -214,14 +201,14 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     const int nrows = skv - k0 < BN ? skv - k0 : BN;
     const unsigned st = lds_u32(smem) + (u % STAGES) * STAGE_B;
     if (wu < 4) {
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(K + (int64_t)k0 * D, nrows * ROWB);
+      const __amdgpu_buffer_rsrc_t r = uniform_rsrc(K + (int64_t)k0 * D, nrows * ROWB);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 4 * wu + i, kbi = j / NDC, c = j % NDC;
         load_lds16(r, k_lane_g, kbi * 32 * ROWB + c * 32, st + j * 1024);
       }
     } else {
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(V + (int64_t)k0 * D, nrows * ROWB);
+      const __amdgpu_buffer_rsrc_t r = uniform_rsrc(V + (int64_t)k0 * D, nrows * ROWB);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 4 * (wu - 4) + i, kc = j / NDB, db = j % NDB;
@@ -433,23 +420,178 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   }
   };
 
-  if (p.persist_c == 0) {
-    // one workgroup per work item, in XCD-aware order
-    const int v = xcd_remap(blockIdx.x, p.work_items);
-    if (v >= 0) run_item(v);
-  } else {
-    // persistent grid: one workgroup per CU (8 XCDs x persist_c CUs; the
-    // work-item count is a multiple of that).  Workgroup g sits on XCD g % 8
-    // and walks that XCD's share of the items in rounds of persist_c,
-    // reversing direction every round, so that a heavy causal tile (items of
-    // a head run heavy first) is paired with a light one.
-    const int C = p.persist_c;
-    const int x = blockIdx.x % 8, c = blockIdx.x / 8;
-    const int per = p.work_items / 8;
-    for (int r = 0; r * C < per; ++r) {
-      run_item(x * per + r * C + ((r & 1) ? C - 1 - c : c));
-      __syncthreads();
+  // ---- scheduling.  Round r of this workgroup names one item through
+  // (tile, sq, skv, off, q_row0, kv_row0); the rounds end when item() returns
+  // false, and skip == true marks an empty item.
+  int a_tile = 0, a_sq = 0, a_skv = 0, a_off = 0;
+  int64_t a_q0 = 0, a_kv0 = 0;
+  // dense item v: (b, h) major, query tiles of a head heaviest first under
+  // a causal mask
+  auto dense_item = [&](const int v) {
+    const int bh = v / p.tiles_per_head;
+    const int rank = v - bh * p.tiles_per_head;
+    const int b = bh / p.H;
+    const int h = bh - b * p.H;
+    a_tile = CAUSAL ? p.tiles_per_head - 1 - rank : rank;
+    a_sq = p.Sq;
+    a_skv = p.Skv;
+    a_off = p.Skv - p.Sq;
+    a_q0 = (int64_t)bh * p.Sq;
+    a_kv0 = ((int64_t)b * p.Hkv + h / p.group) * p.Skv;
+  };
+  // bounds of varlen sequence bb, clamped into [0, T]
+  auto seq_bounds = [&](const int bb, int& s0, int& s1) {
+    const int T = p.Sq;
+    s0 = p.cu[bb];
+    s1 = p.cu[bb + 1];
+    s0 = s0 < 0 ? 0 : (s0 > T ? T : s0);
+    s1 = s1 < s0 ? s0 : (s1 > T ? T : s1);
+  };
+  // query tile `tile` of head h in varlen sequence bb
+  auto seq_item = [&](const int h, const int bb, const int tile) {
+    int s0, s1;
+    seq_bounds(bb, s0, s1);
+    a_tile = tile;
+    a_sq = a_skv = s1 - s0;
+    a_off = 0;
+    a_q0 = (int64_t)h * p.Sq + s0;
+    a_kv0 = (int64_t)(h / p.group) * p.Sq + s0;
+  };
+  // varlen item v: h major, then the concatenated tiles of the sequences,
+  // last first under a causal mask; false for items past the last tile
+  auto varlen_item = [&](const int v) {
+    const int h = v / p.tiles_per_head;
+    int vt = v - h * p.tiles_per_head;
+    if (CAUSAL) vt = p.tiles_per_head - 1 - vt;
+    int acc = 0;
+    for (int bb = 0; bb < p.B; ++bb) {
+      int s0, s1;
+      seq_bounds(bb, s0, s1);
+      const int nt = ceil_div(s1 - s0, BM);
+      if (vt < acc + nt) {
+        seq_item(h, bb, vt - acc);
+        return true;
+      }
+      acc += nt;
     }
+    return false;
+  };
+  // varlen persistent order: XCD x takes the heads [x H/8, (x+1) H/8) (the
+  // query heads of one KV head stay on one L2); its items (sequence, tile,
+  // head) are listed by tile index, highest first (under a causal mask the
+  // cost of a tile grows with its index), then sequence, then head.  The
+  // tiles per sequence are staged in LDS once; cum(t), the number of listed
+  // items with tile index >= t, is (H/8) sum_i max(0, tiles_i - t).
+  const int hpx = p.H / 8;
+  int v_tmax = 0;
+  int64_t v_items = 0;
+  auto wave_sum = [&](int x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+  };
+  auto wave_max = [&](int x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const int y = __shfl_xor(x, m, 64);
+      x = y > x ? y : x;
+    }
+    return x;
+  };
+  auto tiles_at_or_above = [&](const int t) {  // sum_i max(0, tiles_i - t)
+    int acc = 0;
+    for (int i = lane; i < p.B; i += 64) {
+      const int n = seq_tiles[i] - t;
+      acc += n > 0 ? n : 0;
+    }
+    return wave_sum(acc);
+  };
+  if (VARLEN && p.persist_c > 0) {
+    for (int i = tid; i < p.B; i += NT) {
+      int s0, s1;
+      seq_bounds(i, s0, s1);
+      seq_tiles[i] = ceil_div(s1 - s0, BM);
+    }
+    __syncthreads();
+    int mx = 0;
+    for (int i = lane; i < p.B; i += 64) mx = seq_tiles[i] > mx ? seq_tiles[i] : mx;
+    v_tmax = wave_max(mx);
+    v_items = (int64_t)tiles_at_or_above(0) * hpx;
+  }
+  auto listed_item = [&](const int64_t f, const int x) {
+    // level t: cum(t+1) <= f < cum(t); cum falls as t grows
+    int lo = 0, hi = v_tmax - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)tiles_at_or_above(mid) * hpx > f) {
+        lo = mid;
+      } else {
+        hi = mid - 1;
+      }
+    }
+    const int t = lo;
+    const int rr = (int)(f - (int64_t)tiles_at_or_above(t + 1) * hpx);
+    int rank = rr / hpx;
+    const int h = x * hpx + (rr - rank * hpx);
+    // the rank-th sequence (in index order) with more than t tiles
+    for (int i0 = 0; i0 < p.B; i0 += 64) {
+      const int i = i0 + lane;
+      const int ti = seq_tiles[i < p.B ? i : 0];  // every lane reads inside the array
+      uint64_t m = __ballot(i < p.B && ti > t);
+      const int n = __popcll(m);
+      if (rank < n) {
+        for (int k = 0; k < rank; ++k) m &= m - 1;
+        seq_item(h, i0 + __builtin_ctzll(m), t);
+        return;
+      }
+      rank -= n;
+    }
+  };
+  // one workgroup per item (persist_c == 0), or a persistent grid of one
+  // workgroup per CU (8 XCDs x persist_c).  Persistent workgroups take items
+  // in rounds of the grid size, reversing direction every round, so that a
+  // heavy causal tile is paired with a light one.  Workgroup g sits on XCD
+  // g % 8 and walks that XCD's share of the items.  Dense: the host makes the
+  // item count a multiple of the grid.  Varlen: the listed order above; each
+  // item is located by a scan over the sequence lengths (the host enables
+  // this only when that scan is short and H is a multiple of 8).
+  auto item = [&](const int r, bool& skip) {
+    skip = false;
+    if (p.persist_c == 0) {
+      if (r > 0) return false;
+      const int v = xcd_remap(blockIdx.x, p.work_items);
+      if (v < 0) return false;
+      if constexpr (VARLEN) {
+        skip = !varlen_item(v);
+      } else {
+        dense_item(v);
+      }
+      return true;
+    }
+    if constexpr (!VARLEN) {
+      const int C = p.persist_c;
+      const int x = blockIdx.x % 8, c = blockIdx.x / 8;
+      const int per = p.work_items / 8;
+      if (r * C >= per) return false;
+      dense_item(x * per + r * C + ((r & 1) ? C - 1 - c : c));
+    } else {
+      const int C = p.persist_c;
+      const int x = blockIdx.x % 8, c = blockIdx.x / 8;
+      if ((int64_t)r * C >= v_items) return false;
+      const int64_t f = (int64_t)r * C + ((r & 1) ? C - 1 - c : c);
+      if (f >= v_items) {
+        skip = true;
+      } else {
+        listed_item(f, x);
+      }
+    }
+    return true;
+  };
+  for (int r = 0;; ++r) {
+    bool skip;
+    if (!item(r, skip)) break;
+    if (!skip) work(a_tile, a_sq, a_skv, a_off, a_q0, a_kv0);
+    __syncthreads();
   }
 }
 

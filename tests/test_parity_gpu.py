@@ -295,18 +295,28 @@ def test_basic_kernel(case, monkeypatch):
     check(o, lse, o_ref, lse_ref, "bf16", str(case))
 
 
+@pytest.mark.parametrize("varlen", [False, True])
 @pytest.mark.parametrize("causal", [False, True])
-def test_dispatched_grid_matches_persistent(causal, monkeypatch):
-    """The d = 128 kernel runs a persistent grid when the query tiles divide
-    evenly over the CUs; the one-workgroup-per-tile grid (ATTN_NO_PERSIST)
-    must give bitwise the same result."""
+def test_dispatched_grid_matches_persistent(causal, varlen, monkeypatch):
+    """bf16 prefill runs a persistent grid when the query tiles divide evenly
+    over the CUs (dense) or when the sequence scan is short (varlen); the
+    one-workgroup-per-tile grid (ATTN_NO_PERSIST) must give bitwise the same
+    result."""
     import exact_attention_09_amd as ea
-    say(f"persistent vs dispatched, causal={causal}")
-    B, H, S, d = 1, 32, 2048, 128
-    q, k, v = (to_device(synth.normal_tensor(9100 + i, (B, H, S, d), "bf16"), "bf16") for i in range(3))
-    o1, l1 = ea.attn_fwd(q, k, v, causal=causal)
+    say(f"persistent vs dispatched, causal={causal} varlen={varlen}")
+    d = 128
+    if varlen:
+        lengths = (700, 1, 0, 2100, 256, 513, 3000)
+        cu = torch.from_numpy(np.asarray(synth.cu_seqlens_from_lengths(lengths), np.int32)).cuda()
+        T = sum(lengths)
+        q = to_device(synth.normal_tensor(9200, (1, 16, T, d), "bf16"), "bf16")
+        k, v = (to_device(synth.normal_tensor(9201 + i, (1, 4, T, d), "bf16"), "bf16") for i in range(2))
+    else:
+        cu = None
+        q, k, v = (to_device(synth.normal_tensor(9100 + i, (1, 32, 2048, d), "bf16"), "bf16") for i in range(3))
+    o1, l1 = ea.attn_fwd(q, k, v, causal=causal, cu_seqlens=cu)
     monkeypatch.setenv("ATTN_NO_PERSIST", "1")
-    o2, l2 = ea.attn_fwd(q, k, v, causal=causal)
+    o2, l2 = ea.attn_fwd(q, k, v, causal=causal, cu_seqlens=cu)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
