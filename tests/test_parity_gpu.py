@@ -321,6 +321,70 @@ def test_dispatched_grid_matches_persistent(causal, varlen, monkeypatch):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+PERSISTENT = [
+    # (B, H, Hkv, Sq, Skv, d, causal): 256 query tiles of 256 rows, so on a
+    # 256-CU part the persistent grid runs them
+    (2, 16, 4, 2048, 1024, 128, True),    # Sq > Skv: the first 1024 rows see no key
+    (2, 16, 16, 2048, 3000, 128, True),   # Sq < Skv, ragged key tail
+    (1, 32, 8, 2048, 2048, 64, False),
+    (4, 8, 2, 2048, 777, 64, True),
+]
+
+
+def _edge_and_random_rows(B, H, Sq, rng, n=192):
+    fixed = sorted({0, 1, 255, 256, 1023, 1024, Sq // 2, Sq - 2, Sq - 1})
+    rows = [(int(rng.integers(B)), int(rng.integers(H)), i) for i in fixed if 0 <= i < Sq]
+    while len(rows) < n:
+        rows.append((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(Sq))))
+    return np.array(rows, np.int64)
+
+
+@pytest.mark.parametrize("case", PERSISTENT, ids=lambda c: "-".join(map(str, c)))
+def test_persistent_shapes(case):
+    """Persistent-grid prefill (heavy/light pairing, GQA, Sq != Skv, d = 64)
+    against the oracle on sampled rows."""
+    B, H, Hkv, Sq, Skv, d, causal = case
+    say(f"persistent case {case}")
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    q = synth.normal_tensor(seed * 10 + 0, (B, H, Sq, d), "bf16")
+    k = synth.normal_tensor(seed * 10 + 1, (B, Hkv, Skv, d), "bf16")
+    v = synth.normal_tensor(seed * 10 + 2, (B, Hkv, Skv, d), "bf16")
+    scale = 1.0 / math.sqrt(d)
+    o, lse = gpu_run(q, k, v, "bf16", causal, scale)
+    rows = _edge_and_random_rows(B, H, Sq, np.random.default_rng(seed))
+    o_ref, lse_ref = oracle_dense(q, k, v, "bf16", scale, causal, rows=rows)
+    og = np.stack([o[b, h, i] for b, h, i in rows])
+    lg = np.array([lse[b, h, i] for b, h, i in rows])
+    check(og, lg, o_ref, lse_ref, "bf16", str(case))
+
+
+def test_persistent_varlen_many_sequences():
+    """Varlen with 40 sequences (empty, one-token and long ones) on the
+    persistent listed order, against the oracle on sampled rows."""
+    rng = np.random.default_rng(4242)
+    lengths = [0, 1, 2, 255, 256, 257] + [int(x) for x in rng.integers(1, 1500, 34)]
+    H, Hkv, d = 16, 4, 128
+    say(f"persistent varlen, {len(lengths)} sequences, T={sum(lengths)}")
+    T = sum(lengths)
+    cu = synth.cu_seqlens_from_lengths(lengths)
+    q = synth.normal_tensor(5100, (1, H, T, d), "bf16")
+    k = synth.normal_tensor(5101, (1, Hkv, T, d), "bf16")
+    v = synth.normal_tensor(5102, (1, Hkv, T, d), "bf16")
+    scale = 1.0 / math.sqrt(d)
+    o, lse = gpu_run(q, k, v, "bf16", True, scale, cu=cu)
+    rows = []
+    for b, L in enumerate(lengths):
+        for i in sorted({0, L // 2, L - 1}):
+            if 0 <= i < L:
+                rows.append((b, int(rng.integers(H)), i))
+    rows = np.array(rows, np.int64)
+    rf, lf = oracle.attention(host_f32(q, "bf16")[0], host_f32(k, "bf16")[0], host_f32(v, "bf16")[0],
+                              scale, True, cu_seqlens=cu, rows=rows)
+    og = np.stack([o[0, h, cu[b] + i] for b, h, i in rows])
+    lg = np.array([lse[0, h, cu[b] + i] for b, h, i in rows])
+    check(og, lg, rf, lf, "bf16", "persistent varlen")
+
+
 # ------------------------------------------------------------ determinism, canaries
 
 @pytest.mark.parametrize("Sq,ns", [(1, 16), (300, 0)])
