@@ -24,9 +24,10 @@
 //     tile is read during four consecutive slots (K by A then B, V by A then
 //     B two slots later).  Tiles go from HBM straight to LDS (buffer_load ...
 //     lds, no registers on the way), laid out in MFMA fragment order; tile u
-//     is fetched in slot 2(u-PF) into the stage of tile u-PF-2, after the
-//     barrier that ends that tile's last read, and waited for at the end of
-//     slot 2u-1.
+//     is fetched in slots 2(u-PF) (V, by group B) and 2(u-PF)+1 (K, by group
+//     A), each at the start of the loading group's vector phase, into the
+//     stage of tile u-PF-2, after the barrier that ends that tile's last
+//     read, and waited for at the end of slot 2u-1.
 //   * S^T = K Q^T and O^T = V^T P~^T on v_mfma_f32_32x32x16_bf16 (one query
 //     row per lane), K read with ds_read_b128, V with ds_read_b64_tr_b16.
 //     Each fragment read covers one contiguous block (1 KB or 512 B), so it
@@ -240,10 +241,13 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
 
   const int nslots = 2 * nt + 2;
   for (int slot = 0; slot < nslots; ++slot) {
-    // slot 2k fetches tile k+2 into the stage of tile k-2, whose last read
-    // (its V, by group B) was in slot 2k-1; tile k+2 is first read in slot
-    // 2k+4
-    if ((slot & 1) == 0) {
+    // Tile k+PF is fetched into the stage of tile k+PF-STAGES, whose last
+    // read (its V, by group B) was in slot 2k-1: its V blocks by group B in
+    // slot 2k, its K blocks by group A in slot 2k+1, in both cases at the
+    // start of the loading group's vector phase.  (Loads issued by a wave
+    // that is about to run its matrix phase delay that phase's MFMAs, and a
+    // burst from all eight waves at once delays both phases: measured.)
+    if (((slot & 1) == 1) == (wu < 4)) {
       const int k = slot >> 1;
       if (k + PF < nt) load_tile(k + PF);
     }
