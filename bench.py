@@ -6,7 +6,7 @@ reports whole-job TFLOP/s (4*B*H*Sq*Skv*d flop per step), the prefill
 kernel's roofline (MFMA bf16 peak), the fp64 CPU oracle timed on a bounded
 sample of the same workload, and, under "workloads", the other shapes: the
 causal 8K run, the 2K d=64 causal run, varlen grouped-query prefill and
-split-KV decode (HBM roofline).
+split-KV decode over a contiguous and a paged cache (HBM roofline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 """
@@ -97,10 +97,18 @@ def run_workload(name: str, steps: int, warmup: int, inputs=None):
         ns = wl.num_splits or ea.attn_decode_num_splits(wl.B, wl.Hkv, wl.Skv)
         ws = torch.empty(ea.attn_workspace_bytes(wl.B, wl.H, wl.d, ns), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    if wl.paged:
+        bt = torch.from_numpy(x["block_table"]).cuda()
+        sl = torch.from_numpy(x["seqlens_k"]).cuda()
+        lse = torch.empty((wl.B, wl.H), dtype=torch.float32, device=q.device)
 
-    def step():
-        ea.attn_fwd_ex(q, k, v, o, lse, causal=wl.causal, scale=wl.scale, cu_seqlens=cu, num_splits=ns,
-                       workspace=ws, stream=stream.cuda_stream)
+        def step():
+            ea.attn_fwd_paged(q, k, v, bt, sl, o, lse, scale=wl.scale, num_splits=ns, workspace=ws,
+                              stream=stream.cuda_stream)
+    else:
+        def step():
+            ea.attn_fwd_ex(q, k, v, o, lse, causal=wl.causal, scale=wl.scale, cu_seqlens=cu, num_splits=ns,
+                           workspace=ws, stream=stream.cuda_stream)
 
     t = time_steps(step, steps, warmup, stream)
     del q, k, v, o, lse, ws
@@ -200,7 +208,7 @@ def main(argv=None):
     workloads = {}
     if not args.quick:
         for name in ("mha_causal_s8192_d128", "mha_causal_s2048_d64", "varlen_gqa_causal_d128",
-                     "decode_gqa_s16384_d128"):
+                     "decode_gqa_s16384_d128", "decode_paged_gqa_s16384_d128"):
             print(f"# timing {name}", file=sys.stderr, flush=True)
             w, ns, tt = run_workload(name, args.steps, args.warmup)
             entry = {"ms_per_step": round(tt["wall_ms_per_step"], 4), "launch_ms_mean": round(tt["event_ms_mean"], 4)}

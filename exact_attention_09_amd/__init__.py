@@ -11,6 +11,8 @@ Names mirror the C entry points:
 * ``attn_fwd`` (bf16), ``attn_fwd_f32`` (fp32), ``attn_fwd_ex`` (either, with
   split-KV options) take torch tensors on the GPU in BHSD layout and return
   ``(o, lse)``;
+* ``attn_fwd_paged`` runs split-KV decode over a paged KV cache (block
+  table and per-sequence key counts) and returns ``(o, lse)``;
 * ``attn_workspace_bytes``, ``attn_decode_num_splits``,
   ``attn_status_string``, ``attn_last_error`` are the helpers.
 """
@@ -27,7 +29,7 @@ ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ENOMEM, ATTN_EHIP = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
 ATTN_MAX_SPLITS = 256
 
-EXPORTED = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_workspace_bytes",
+EXPORTED = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_paged", "attn_workspace_bytes",
             "attn_decode_num_splits", "attn_status_string", "attn_last_error")
 
 
@@ -62,6 +64,9 @@ def load_library(path: str = LIB_PATH):
         fn.argtypes = fwd_args
     lib.attn_fwd_ex.restype = ctypes.c_int
     lib.attn_fwd_ex.argtypes = fwd_args + [ctypes.c_int, ctypes.POINTER(AttnOpts)]
+    lib.attn_fwd_paged.restype = ctypes.c_int
+    lib.attn_fwd_paged.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 7 + [
+        ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(AttnOpts)]
     lib.attn_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_workspace_bytes.argtypes = [ctypes.c_int] * 4
     lib.attn_decode_num_splits.restype = ctypes.c_int
@@ -157,6 +162,54 @@ def attn_fwd_ex(q, k, v, o=None, lse=None, *, causal: bool = False, scale: float
     st = lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Sq, Skv, d,
                          float(scale), int(bool(causal)), _ptr(cu_seqlens), ctypes.c_void_p(stream),
                          int(dtype), ctypes.byref(opts))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_last_error())
+    return o, lse
+
+
+def attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, o=None, lse=None, *,
+                   scale: float | None = None, num_splits: int = 0, workspace=None, stream=None,
+                   want_lse: bool = True):
+    """Split-KV decode over a paged KV cache through ``attn_fwd_paged``.
+
+    q [B,H,1,d] (or [B,H,d]) bf16; k_cache/v_cache [num_pages,Hkv,page_size,d]
+    bf16; block_table [B,max_pages] int32 and seqlens_k [B] int32 on the GPU.
+    Returns ``(o, lse)`` with o shaped like q and lse [B,H] (or None).
+    """
+    import torch
+    lib = load_library()
+    if q.dim() == 3:
+        q = q.unsqueeze(2)
+    if q.dim() != 4 or q.shape[2] != 1:
+        raise ValueError("q is [B, H, 1, d]")
+    B, H, _, d = q.shape
+    if k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache are [num_pages, Hkv, page_size, d]")
+    num_pages, Hkv, page_size, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("cache head dim differs from q's")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor on the GPU")
+    for name, t in (("block_table", block_table), ("seqlens_k", seqlens_k)):
+        if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous int32 tensor on the GPU")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seqlens_k.numel() != B:
+        raise ValueError("block_table is [B, max_pages] and seqlens_k is [B]")
+    max_pages = block_table.shape[1]
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    opts = AttnOpts(int(num_splits), workspace.data_ptr() if workspace is not None else None,
+                    workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    st = lib.attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(block_table),
+                            _ptr(seqlens_k), B, H, Hkv, d, page_size, max_pages, num_pages, float(scale),
+                            ctypes.c_void_p(stream), ctypes.byref(opts))
     if st != ATTN_OK:
         raise AttnError(st, attn_last_error())
     return o, lse

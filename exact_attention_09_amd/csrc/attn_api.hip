@@ -217,6 +217,92 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
   return status;
 }
 
+attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                           const int32_t* block_table, const int32_t* seqlens_k, int B, int H, int Hkv,
+                           int d, int page_size, int max_pages, int num_pages, float scale, void* stream,
+                           const attn_opts* opts) {
+  g_err[0] = '\0';
+  // ---- validation: no HIP call until every check has passed
+  if (B < 0 || H < 0 || Hkv < 0 || d < 0 || max_pages < 0 || num_pages < 0)
+    return fail(ATTN_EINVAL, "negative size (B=%d H=%d Hkv=%d d=%d max_pages=%d num_pages=%d)", B, H, Hkv, d,
+                max_pages, num_pages);
+  if (opts != nullptr && (opts->num_splits < 0 || opts->num_splits > ATTN_MAX_SPLITS))
+    return fail(ATTN_EINVAL, "num_splits %d outside [0, %d]", opts->num_splits, ATTN_MAX_SPLITS);
+  if (B == 0 || H == 0) return ATTN_OK;  // nothing to compute
+  if (q == nullptr || o == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+      seqlens_k == nullptr)
+    return fail(ATTN_EINVAL, "q, o, k_cache, v_cache, block_table and seqlens_k must not be NULL");
+  if (Hkv < 1 || H % Hkv != 0) return fail(ATTN_EINVAL, "H=%d is not a multiple of Hkv=%d", H, Hkv);
+  if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "head dim %d (built: 64, 128)", d);
+  if (page_size < 16 || page_size > (1 << 16) || (page_size & (page_size - 1)) != 0)
+    return fail(ATTN_EUNSUPPORTED, "page size %d (built: powers of two from 16 to 65536)", page_size);
+  if (max_pages < 1 || num_pages < 1) return fail(ATTN_EINVAL, "max_pages and num_pages must be >= 1");
+  if ((long)max_pages * page_size > 0x7fffffffL)
+    return fail(ATTN_EINVAL, "max_pages * page_size = %ld keys does not fit int32", (long)max_pages * page_size);
+  if ((long double)num_pages * Hkv * page_size * d > 9.0e18L) return fail(ATTN_EINVAL, "cache too large");
+  if (!(std::isfinite(scale) && scale > 0.0f))
+    return fail(ATTN_EINVAL, "scale must be finite and > 0 (got %g)", (double)scale);
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16))
+    return fail(ATTN_EINVAL, "q, k_cache, v_cache, o must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seqlens_k, 4) || (lse != nullptr && !aligned(lse, 4)))
+    return fail(ATTN_EINVAL, "block_table, seqlens_k and lse must be 4-byte aligned");
+
+  attn::Params p{};
+  p.q = q; p.k = k_cache; p.v = v_cache; p.o = o; p.lse = lse;
+  p.B = B; p.H = H; p.Hkv = Hkv; p.Sq = 1; p.Skv = max_pages * page_size; p.d = d;
+  p.group = H / Hkv;
+  p.scale = scale;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  p.block_table = block_table;
+  p.seqlens_k = seqlens_k;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  p.page_shift = shift;
+  p.max_pages = max_pages;
+  p.num_pages = num_pages;
+  hipStream_t st = (hipStream_t)stream;
+
+  int splits = (opts != nullptr && opts->num_splits > 0) ? opts->num_splits : attn_decode_num_splits(B, Hkv, p.Skv);
+  if (splits > p.Skv) splits = p.Skv;
+  if (splits < 1) splits = 1;
+  p.num_splits = splits;
+  p.tiles_per_head = 1;
+  if ((long)B * H * splits > 0x7ffffff0L) return fail(ATTN_EINVAL, "too many decode rows");
+  const size_t need = attn_workspace_bytes(B, H, d, splits);
+  const long rows = (long)B * H;
+  void* ws = nullptr;
+  bool own = false;
+  if (opts != nullptr && opts->workspace != nullptr) {
+    if (opts->workspace_bytes < need)
+      return fail(ATTN_EINVAL, "workspace of %zu bytes, %zu needed", opts->workspace_bytes, need);
+    if (!aligned(opts->workspace, kWsAlign)) return fail(ATTN_EINVAL, "workspace must be 256-byte aligned");
+    ws = opts->workspace;
+  } else {
+    const hipError_t e = hipMallocAsync(&ws, need, st);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(ATTN_ENOMEM, "workspace of %zu bytes: %s", need, hipGetErrorString(e));
+    }
+    own = true;
+  }
+  p.ws_o = (float*)ws;
+  p.ws_lse = (float*)((char*)ws + ws_lse_offset(rows, d, splits));
+
+  hipError_t e = attn::launch_decode_bf16(p, st);
+  attn_status status = ATTN_OK;
+  if (e != hipSuccess) {
+    status = hip_fail(e, "paged split kernel");
+  } else {
+    e = attn::launch_combine(p, true, st);
+    if (e != hipSuccess) status = hip_fail(e, "combine kernel");
+  }
+  if (own) {
+    const hipError_t ef = hipFreeAsync(ws, st);
+    if (ef != hipSuccess && status == ATTN_OK) status = hip_fail(ef, "workspace release");
+  }
+  return status;
+}
+
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int H, int Hkv, int Sq, int Skv, int d, float scale, int causal,
                      const int32_t* cu_seqlens, void* stream) {

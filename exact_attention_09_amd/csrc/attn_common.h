@@ -30,6 +30,12 @@ struct Params {
   int tiles_per_head;      // query tiles per (b, h) (varlen: upper bound per head)
   int work_items;          // real work items; the grid may be padded to 8k
   int persist_c;           // > 0: persistent grid of 8 x persist_c workgroups (see the kernel)
+  // paged KV cache (decode): k and v are [num_pages, Hkv, page_size, d]
+  const int32_t* block_table;  // [B, max_pages] physical page of each logical block, or null
+  const int32_t* seqlens_k;    // [B] keys per sequence
+  int page_shift;              // log2(page_size)
+  int max_pages;               // row length of block_table
+  int num_pages;               // pages in the cache (table entries are clamped into range)
 };
 
 // ---------------------------------------------------------------- helpers

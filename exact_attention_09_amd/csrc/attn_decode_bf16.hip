@@ -19,6 +19,16 @@
 //   * the next chunk's loads are in flight while the current chunk is used;
 //   * the four waves' (m, l, O) states are merged through LDS in fixed order
 //     at the end, so the result is bitwise reproducible.
+//
+// Paged KV cache (PAGED): the keys of sequence b are read through its block
+// table, key t from physical page block_table[b][t / page_size] at offset
+// t % page_size (tutorial section 4.8 (2); the CUDA course chapter 12,
+// section 12.9.4); the cache is [num_pages, Hkv, page_size, d], so the rows
+// of one (page, KV head) are contiguous.  Sequence b has seqlens_k[b] keys and
+// its splits are ceil(seqlens_k[b] / num_splits) keys long.  Table entries
+// and lengths are clamped into range, so a malformed table gives wrong
+// numbers, never an out-of-bounds access.  Nothing else changes: the
+// indirection decides where the bytes come from, not what is computed.
 #include "attn_common.h"
 #include "attn_internal.h"
 
@@ -28,7 +38,7 @@ namespace {
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void decode_split_bf16_kernel(const Params p) {
   constexpr int NW = 4;
   constexpr int NDC = D / 32;       // contraction steps of QK^T (32 d each)
@@ -56,9 +66,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16_kernel(const Params 
   const int kvh = w % p.Hkv;
   const int b = w / p.Hkv;
 
-  const int lo = s * p.split_len;
-  int hi = lo + p.split_len;
-  hi = hi < p.Skv ? hi : p.Skv;
+  int skv = p.Skv, split_len = p.split_len;
+  if constexpr (PAGED) {
+    const int cap = p.max_pages << p.page_shift;
+    skv = p.seqlens_k[b];
+    skv = skv < 0 ? 0 : (skv > cap ? cap : skv);
+    split_len = ceil_div(skv, S);
+  }
+  const int lo = s * split_len;
+  int hi = lo + split_len;
+  hi = hi < skv ? hi : skv;
   const int nchunks = hi > lo ? ceil_div(hi - lo, 32) : 0;
 
   const int hl = hgp * 16 + l16;         // this lane's query head within the group
@@ -66,9 +83,20 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16_kernel(const Params 
   const int h = kvh * p.group + (qvalid ? hl : 0);
 
   const __bf16* __restrict__ Q = (const __bf16*)p.q + ((int64_t)b * p.H + h) * D;
-  const int64_t kv0 = ((int64_t)b * p.Hkv + kvh) * p.Skv;
+  const int64_t kv0 = PAGED ? 0 : ((int64_t)b * p.Hkv + kvh) * p.Skv;
   const __bf16* __restrict__ K = (const __bf16*)p.k + kv0 * D;
   const __bf16* __restrict__ V = (const __bf16*)p.v + kv0 * D;
+  const int32_t* __restrict__ table = PAGED ? p.block_table + (int64_t)b * p.max_pages : nullptr;
+  // row of key `key` (< skv) relative to K and V
+  auto key_row = [&](const int key) -> int64_t {
+    if constexpr (PAGED) {
+      int page = table[key >> p.page_shift];
+      page = page < 0 ? 0 : (page >= p.num_pages ? p.num_pages - 1 : page);
+      return (((int64_t)page * p.Hkv + kvh) << p.page_shift) + (key & ((1 << p.page_shift) - 1));
+    } else {
+      return key;
+    }
+  };
 
   // Q^T as the B operand: column l16 = head, d = 32c + 8kg + j
   bf16x8 qf[NDC];
@@ -84,10 +112,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16_kernel(const Params 
     for (int kb = 0; kb < 2; ++kb) {
       int key = lo + 32 * ci + 16 * kb + l16;
       key = key < hi ? key : hi - 1;
+      const int64_t row = key_row(key);
 #pragma unroll
       for (int c = 0; c < NDC; ++c) {
-        kr[kb][c] = *(const u32x4*)(K + (int64_t)key * D + 32 * c + 8 * kg);
-        vr[kb][c] = *(const u32x4*)(V + (int64_t)key * D + 32 * c + 8 * kg);
+        kr[kb][c] = *(const u32x4*)(K + row * D + 32 * c + 8 * kg);
+        vr[kb][c] = *(const u32x4*)(V + row * D + 32 * c + 8 * kg);
       }
     }
   };
@@ -247,10 +276,18 @@ hipError_t launch_decode_bf16(const Params& p, hipStream_t st) {
   const long grid = (long)p.B * p.Hkv * HG * p.num_splits;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  if (p.d == 128)
-    hipLaunchKernelGGL(decode_split_bf16_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL(decode_split_bf16_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, p);
+  const bool paged = p.block_table != nullptr;
+  if (p.d == 128) {
+    if (paged)
+      hipLaunchKernelGGL((decode_split_bf16_kernel<128, true>), dim3((unsigned)grid), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((decode_split_bf16_kernel<128, false>), dim3((unsigned)grid), dim3(256), 0, st, p);
+  } else {
+    if (paged)
+      hipLaunchKernelGGL((decode_split_bf16_kernel<64, true>), dim3((unsigned)grid), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((decode_split_bf16_kernel<64, false>), dim3((unsigned)grid), dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 

@@ -18,7 +18,12 @@ Generator (counter based, so any slice can be produced independently):
   workloads, from fp32 to bf16 (round to nearest even on the fp32 bit pattern).
 
 Seeds: ``1000 * workload_id + tensor_id`` with tensor ids Q=0, K=1, V=2,
-sequence lengths=3.
+sequence lengths=3, page tables=4.
+
+Page tables (paged KV caches): the physical pages are a seeded random
+permutation (the order of the stream outputs ``0 .. num_pages-1``, ties broken
+by index), dealt out to the sequences in order, so that consecutive logical
+blocks of a sequence sit in scattered physical pages.
 """
 
 from __future__ import annotations
@@ -32,7 +37,7 @@ GOLDEN_GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_LENGTHS = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_LENGTHS, TENSOR_PAGES = 0, 1, 2, 3, 4
 
 _CHUNK = 1 << 22  # normals per work item
 
@@ -124,3 +129,18 @@ def cu_seqlens_from_lengths(lengths) -> np.ndarray:
     if cu[-1] > np.iinfo(np.int32).max:
         raise ValueError("total length does not fit int32")
     return cu.astype(np.int32)
+
+
+def page_permutation(seed: int, num_pages: int) -> np.ndarray:
+    """A seeded random permutation of ``0 .. num_pages-1`` (int64)."""
+    x = splitmix64(seed, 0, num_pages)
+    return np.argsort(x, kind="stable").astype(np.int64)
+
+
+def page_table(seed: int, B: int, max_pages: int, num_pages: int) -> np.ndarray:
+    """int32 [B, max_pages] block table: row b holds the physical pages
+    ``perm[b * max_pages .. (b + 1) * max_pages)`` of a random permutation."""
+    if B * max_pages > num_pages:
+        raise ValueError("not enough physical pages for the table")
+    perm = page_permutation(seed, num_pages)
+    return perm[:B * max_pages].reshape(B, max_pages).astype(np.int32)

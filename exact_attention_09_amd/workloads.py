@@ -2,7 +2,8 @@
 
 Shapes are the ones the pages' discussion is built around (a single head for
 the worked examples, multi-head prefill at 2K and 8K tokens, packed
-variable-length grouped-query prefill, and split-KV decode over a 16K cache).
+variable-length grouped-query prefill, and split-KV decode over a 16K cache,
+contiguous or paged).
 Inputs are synthetic i.i.d. N(0, 1) from ``synth`` with seed
 ``1000 * workload_id + tensor_id``.
 
@@ -37,6 +38,23 @@ class Workload:
     causal: bool
     lengths: tuple = field(default=())   # varlen sequence lengths (then B = len)
     num_splits: int = 0      # decode path split count (0 = library heuristic)
+    page_size: int = 0       # > 0: decode over a paged KV cache of Skv keys per sequence
+
+    @property
+    def paged(self) -> bool:
+        return self.page_size > 0
+
+    @property
+    def max_pages(self) -> int:
+        return -(-self.Skv // self.page_size) if self.paged else 0
+
+    @property
+    def num_pages(self) -> int:
+        # one spare page per sequence, so the table is not the whole cache
+        return self.B * (self.max_pages + 1) if self.paged else 0
+
+    def cache_shape(self):
+        return (self.num_pages, self.Hkv, self.page_size, self.d)
 
     @property
     def varlen(self) -> bool:
@@ -58,6 +76,8 @@ class Workload:
         return (1, self.H, self.total_tokens, self.d) if self.varlen else (self.B, self.H, self.Sq, self.d)
 
     def kv_shape(self):
+        if self.paged:
+            return self.cache_shape()
         return (1, self.Hkv, self.total_tokens, self.d) if self.varlen else (self.B, self.Hkv, self.Skv, self.d)
 
     def cu_seqlens(self):
@@ -77,6 +97,8 @@ class Workload:
         eb = self.elem_bytes
         q_o = 2 * int(np.prod(self.q_shape())) * eb
         kv = 2 * int(np.prod(self.kv_shape())) * eb
+        if self.paged:  # the pages the sequences use, not the whole pool
+            kv = 2 * self.B * self.Hkv * self.Skv * self.d * eb
         lse = 4 * self.rows()
         partial = 0
         if num_splits and not self.varlen and self.Sq == 1:
@@ -90,7 +112,12 @@ class Workload:
         q = synth.normal_tensor(base + synth.TENSOR_Q, self.q_shape(), self.dtype)
         k = synth.normal_tensor(base + synth.TENSOR_K, self.kv_shape(), self.dtype)
         v = synth.normal_tensor(base + synth.TENSOR_V, self.kv_shape(), self.dtype)
-        return {"q": q, "k": k, "v": v, "cu_seqlens": self.cu_seqlens()}
+        out = {"q": q, "k": k, "v": v, "cu_seqlens": self.cu_seqlens()}
+        if self.paged:
+            out["block_table"] = synth.page_table(base + synth.TENSOR_PAGES, self.B, self.max_pages,
+                                                  self.num_pages)
+            out["seqlens_k"] = np.full(self.B, self.Skv, np.int32)
+        return out
 
 
 def host_f32(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -124,4 +151,9 @@ WORKLOADS = {
                                        causal=True, lengths=VARLEN_LENGTHS),
     "decode_gqa_s16384_d128": Workload("decode_gqa_s16384_d128", 5, B=32, H=32, Hkv=8, Sq=1, Skv=16384, d=128,
                                        dtype="bf16", causal=False, num_splits=16),
+    # the same decode over a paged cache: 16-token pages (the CUDA course's
+    # typical block size) scattered by a seeded permutation
+    "decode_paged_gqa_s16384_d128": Workload("decode_paged_gqa_s16384_d128", 6, B=32, H=32, Hkv=8, Sq=1,
+                                             Skv=16384, d=128, dtype="bf16", causal=False, num_splits=16,
+                                             page_size=16),
 }

@@ -117,6 +117,36 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
                         const int32_t* cu_seqlens, void* stream, attn_dtype dtype,
                         const attn_opts* opts);
 
+/* Split-KV decode over a paged KV cache: one query row per head (Sq == 1),
+ * bf16.  A paged cache changes where the key and value bytes live, not what
+ * is computed (tutorial section 4.8 (2)): the cache is cut into pages of
+ * page_size tokens and block_table maps logical block j of sequence b to a
+ * physical page, key t living in page block_table[b * max_pages +
+ * t / page_size] at offset t % page_size (the CUDA course chapter 12,
+ * section 12.9.4).
+ *
+ *   q, o        : [B, H, 1, d] bf16          lse: [B, H] fp32 (may be NULL)
+ *   k_cache,
+ *   v_cache     : [num_pages, Hkv, page_size, d] bf16 (head-major pages)
+ *   block_table : [B, max_pages] int32, entries in [0, num_pages)
+ *   seqlens_k   : [B] int32, keys of sequence b, in [0, max_pages*page_size]
+ *
+ * page_size must be a power of two from 16 to 65536 (the CUDA course asks
+ * for multiples of 16; powers of two keep the page arithmetic to shifts),
+ * else ATTN_EUNSUPPORTED.  Device-side entries are clamped into range, so a
+ * malformed table or length gives wrong numbers, never an out-of-bounds
+ * access.  A sequence with no key gets O = 0 and LSE = -inf.  Splits: each
+ * sequence's keys are cut into num_splits chunks of
+ * ceil(seqlens_k[b] / num_splits) keys and combined as in attn_fwd's decode
+ * path; opts (may be NULL) gives the split count and the workspace
+ * (attn_workspace_bytes(B, H, d, num_splits) bytes), with the same rules.
+ * Validation, errors, ownership and ordering on `stream` are as for
+ * attn_fwd_ex. */
+attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                           const int32_t* block_table, const int32_t* seqlens_k, int B, int H, int Hkv,
+                           int d, int page_size, int max_pages, int num_pages, float scale, void* stream,
+                           const attn_opts* opts);
+
 /* Bytes of workspace the decode path needs for B, H, d and num_splits
  * (fp32 partial outputs [B,H,splits,d] and base-2 LSEs [B,H,splits]).
  * Returns 0 for invalid sizes. */

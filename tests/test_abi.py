@@ -109,3 +109,38 @@ def test_decode_split_heuristic(lib, monkeypatch):
 def test_status_strings(lib):
     assert ea.attn_status_string(ea.ATTN_OK) == "ok"
     assert "unsupported" in ea.attn_status_string(ea.ATTN_EUNSUPPORTED)
+
+
+def paged_call(lib, *, q=P, kc=P, vc=P, o=Q2, lse=None, bt=P, sl=P, B=2, H=4, Hkv=2, d=128, page_size=16,
+               max_pages=4, num_pages=8, scale=0.1, opts=None):
+    return lib.attn_fwd_paged(q, kc, vc, o, lse, bt, sl, B, H, Hkv, d, page_size, max_pages, num_pages, scale,
+                              None, ctypes.byref(opts) if opts is not None else None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ea.ATTN_EINVAL),
+    (dict(kc=None), ea.ATTN_EINVAL),
+    (dict(vc=None), ea.ATTN_EINVAL),
+    (dict(bt=None), ea.ATTN_EINVAL),
+    (dict(sl=None), ea.ATTN_EINVAL),
+    (dict(H=6, Hkv=4), ea.ATTN_EINVAL),
+    (dict(d=80), ea.ATTN_EUNSUPPORTED),
+    (dict(page_size=8), ea.ATTN_EUNSUPPORTED),
+    (dict(page_size=48), ea.ATTN_EUNSUPPORTED),
+    (dict(max_pages=0), ea.ATTN_EINVAL),
+    (dict(num_pages=0), ea.ATTN_EINVAL),
+    (dict(max_pages=1 << 20, page_size=4096), ea.ATTN_EINVAL),
+    (dict(scale=-1.0), ea.ATTN_EINVAL),
+    (dict(kc=ctypes.c_void_p(0x100004)), ea.ATTN_EINVAL),
+    (dict(bt=ctypes.c_void_p(0x100002)), ea.ATTN_EINVAL),
+    (dict(opts=ea.AttnOpts(ea.ATTN_MAX_SPLITS + 1, None, 0)), ea.ATTN_EINVAL),
+    (dict(opts=ea.AttnOpts(4, 0x500000, 16)), ea.ATTN_EINVAL),
+])
+def test_paged_rejects_before_any_hip_call(lib, kw, status):
+    assert paged_call(lib, **kw) == status
+    assert ea.attn_last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(B=0, q=None, kc=None, vc=None, o=None, bt=None, sl=None)])
+def test_paged_empty_problem_is_a_no_op(lib, kw):
+    assert paged_call(lib, **kw) == ea.ATTN_OK
