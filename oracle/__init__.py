@@ -48,7 +48,8 @@ def load(path: str = LIB_PATH):
     fn.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int,
                                                                 ctypes.c_void_p, ctypes.c_void_p,
                                                                 ctypes.c_int64, ctypes.c_void_p,
-                                                                ctypes.c_void_p, ctypes.c_int]
+                                                                ctypes.c_void_p, ctypes.c_int,
+                                                                ctypes.c_int, ctypes.c_void_p]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -59,12 +60,15 @@ def _f32(x) -> np.ndarray:
 
 
 def attention(q, k, v, scale: float, causal: bool = False, cu_seqlens=None, rows=None,
-              nthreads: int | None = None, lib=None):
+              nthreads: int | None = None, lib=None, window: int = 0, sinks=None):
     """Exact attention in fp64.
 
     Dense: q [B,H,Sq,d], k/v [B,Hkv,Skv,d].  Varlen (``cu_seqlens`` given, B+1
     int32): q [H,T,d] (or [1,H,T,d]), k/v [Hkv,T,d].  Inputs are any float
     arrays whose values fp32 holds exactly (fp32 or widened bf16).
+    ``window`` > 0 keeps the last ``window`` keys up to the (bottom-right)
+    diagonal; ``sinks`` ([H] logits) adds exp(sink - m) to each row's
+    denominator.
 
     Returns ``(o, lse)`` as fp64 in the output layout, or for ``rows`` (an
     [n,3] array of (b, h, i)) as [n,d] and [n].
@@ -100,9 +104,13 @@ def attention(q, k, v, scale: float, causal: bool = False, cu_seqlens=None, rows
         lse = np.empty(lse_shape, np.float64)
         rows_ptr = None
     nthreads = nthreads or (os.cpu_count() or 1)
+    sk = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.float64).reshape(-1)
+    if sk is not None and sk.shape[0] != H:
+        raise ValueError("sinks must hold one value per query head")
     st = lib.oracle_attn_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Hkv, Sq, Skv, d,
                              float(scale), int(bool(causal)), cu_ptr, rows_ptr, n,
-                             o.ctypes.data, lse.ctypes.data, int(nthreads))
+                             o.ctypes.data, lse.ctypes.data, int(nthreads), int(window),
+                             None if sk is None else sk.ctypes.data)
     if st != 0:
         raise ValueError(f"oracle_attn_f64 failed with status {st}")
     return o, lse

@@ -17,6 +17,14 @@
  *   - same page, section 4.8 (1): query head h reads KV head h / (H / Hkv).
  *   - "learn-cuda-from-scratch" ch.12, FA3 skeleton: the log-sum-exp output is
  *     m + log(l) in the natural base, of the scaled scores.
+ *   - sliding window (TileLang tutorial section 5.2; the CUDA course ch.12,
+ *     section 12.9.5): with window W > 0 key j is visible to query i iff
+ *     i + (Skv - Sq) - W < j <= i + (Skv - Sq), the causal bound included.
+ *   - attention sink (TileLang tutorial sections 4.6 and 4.7): a per-head
+ *     logit that joins the softmax denominator only, exp(sink - m) added to
+ *     l, with m taken as max(row max, sink) so that a large sink cannot
+ *     overflow; the log-sum-exp then includes the sink.  A row that sees no
+ *     key but has a sink gets O = 0 and LSE = sink.
  *
  * For each row the scores of every visible key are materialised in an fp64
  * buffer, the maximum m is taken, p_j = exp(s_j - m), l = sum p_j,
@@ -33,6 +41,8 @@
 typedef struct {
   const float *q, *k, *v;
   int B, H, Hkv, Sq, Skv, d, causal;
+  int window;            /* > 0: sliding window of this many keys (causal implied) */
+  const double* sinks;   /* NULL, or one logit per query head */
   double scale;
   const int32_t* cu;  /* NULL: dense batch */
   const int64_t* rows; /* NULL: every row */
@@ -116,38 +126,49 @@ static void* worker(void* arg) {
       double* out = J->o + (J->rows ? r : orow) * d;
       double* lout = J->lse ? J->lse + (J->rows ? r : orow) : NULL;
 
-      /* visible keys: j < skv, and j <= i + (skv - sq) when causal */
+      /* visible keys: jlo <= j < nvis; j < skv, j <= i + (skv - sq) when
+         causal (or windowed), j > i + (skv - sq) - window with a window */
       int64_t nvis = skv;
-      if (J->causal) {
+      if (J->causal || J->window > 0) {
         int64_t lim = (int64_t)i + (skv - sq) + 1;
         if (lim < nvis) nvis = lim;
         if (nvis < 0) nvis = 0;
       }
-      if (nvis == 0) {
+      int64_t jlo = 0;
+      if (J->window > 0) {
+        jlo = (int64_t)i + (skv - sq) - J->window + 1;
+        if (jlo < 0) jlo = 0;
+      }
+      const double sink = J->sinks ? J->sinks[h] : -INFINITY;
+      if (nvis <= jlo) {
         for (int t = 0; t < d; ++t) out[t] = 0.0;
         if (lout) *lout = -INFINITY;
+        if (lout && J->sinks) *lout = sink; /* l = exp(sink - sink) = 1 */
         continue;
       }
-      /* materialise the scaled scores of the row */
+      const int64_t n = nvis - jlo;
+      /* materialise the scaled scores of the row (s[j] is key jlo + j) */
       double m = -INFINITY;
-      for (int64_t j = 0; j < nvis; ++j) {
-        const float* krow = kbase + j * d;
+      for (int64_t j = 0; j < n; ++j) {
+        const float* krow = kbase + (jlo + j) * d;
         double dot = 0.0;
         for (int t = 0; t < d; ++t) dot += (double)qrow[t] * (double)krow[t];
         s[j] = J->scale * dot;
         if (s[j] > m) m = s[j];
       }
-      /* safe softmax: p_j = exp(s_j - m), l = sum p_j */
+      if (J->sinks && sink > m) m = sink; /* m* = max(row max, sink) */
+      /* safe softmax: p_j = exp(s_j - m), l = sum p_j (+ the sink's term) */
       double l = 0.0;
-      for (int64_t j = 0; j < nvis; ++j) {
+      for (int64_t j = 0; j < n; ++j) {
         s[j] = exp(s[j] - m);
         l += s[j];
       }
+      if (J->sinks) l += exp(sink - m);
       /* O = sum_j (p_j / l) v_j */
       for (int t = 0; t < d; ++t) acc[t] = 0.0;
-      for (int64_t j = 0; j < nvis; ++j) {
+      for (int64_t j = 0; j < n; ++j) {
         const double w = s[j] / l;
-        const float* vrow = vbase + j * d;
+        const float* vrow = vbase + (jlo + j) * d;
         for (int t = 0; t < d; ++t) acc[t] += w * (double)vrow[t];
       }
       for (int t = 0; t < d; ++t) out[t] = acc[t];
@@ -166,13 +187,16 @@ static void* worker(void* arg) {
  * sequence attends to itself (Sq_b = Skv_b); Sq, Skv are ignored.
  * rows: optional list of nrows (b, h, i) triples (i is the row inside its
  * sequence); then o is [nrows,d] and lse [nrows].
+ * window: 0, or a sliding window of that many keys (the causal bound is
+ * implied); sinks: NULL, or H per-query-head logits.
  * Returns 0 on success, 1 on invalid arguments, 3 when memory runs out.
  */
 int oracle_attn_f64(const float* q, const float* k, const float* v, int B, int H, int Hkv,
                     int Sq, int Skv, int d, double scale, int causal,
                     const int32_t* cu_seqlens, const int64_t* rows, int64_t nrows, double* o,
-                    double* lse, int nthreads) {
+                    double* lse, int nthreads, int window, const double* sinks) {
   if (B < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || d <= 0 || !q || !k || !v || !o) return 1;
+  if (window < 0) return 1;
   if (!cu_seqlens && (Sq < 0 || Skv < 0)) return 1;
   if (cu_seqlens) {
     if (cu_seqlens[0] != 0) return 1;
@@ -202,6 +226,7 @@ int oracle_attn_f64(const float* q, const float* k, const float* v, int B, int H
     J->q = q; J->k = k; J->v = v;
     J->B = B; J->H = H; J->Hkv = Hkv; J->Sq = Sq; J->Skv = Skv; J->d = d;
     J->causal = causal; J->scale = scale; J->cu = cu_seqlens;
+    J->window = window; J->sinks = sinks;
     J->rows = rows; J->nrows = nrows; J->o = o; J->lse = lse;
     J->tid = t; J->nthreads = nthreads; J->status = 0;
   }

@@ -220,6 +220,88 @@ def pin_row_subset(lib):
         assert np.array_equal(orow[r], o[b, h, i]) and lrow[r] == lse[b, h, i]
 
 
+# ----------------------------------------------------- sliding window, sinks
+
+def pin_window_is_key_slice(lib):
+    """With a window W, row i equals unmasked attention over the keys
+    (i + off - W, i + off], off = Skv - Sq (the tutorial's section 5.2 band,
+    bottom-right aligned); rows with no key in the band are empty."""
+    rng = np.random.default_rng(19)
+    for sq, skv, w in [(9, 9, 3), (5, 12, 4), (12, 7, 2), (6, 6, 1)]:
+        q = rng_tensor(rng, (1, 2, sq, 8)); k = rng_tensor(rng, (1, 2, skv, 8)); v = rng_tensor(rng, (1, 2, skv, 8))
+        o, lse = oracle.attention(q, k, v, 0.6, True, window=w, lib=lib)
+        off = skv - sq
+        for i in range(sq):
+            lo, hi = max(0, i + off - w + 1), min(skv, i + off + 1)
+            if hi <= lo:
+                assert np.all(o[0, :, i] == 0.0) and np.all(np.isneginf(lse[0, :, i]))
+                continue
+            oi, li = oracle.attention(q[:, :, i:i + 1], k[:, :, lo:hi], v[:, :, lo:hi], 0.6, lib=lib)
+            assert np.array_equal(o[0, :, i], oi[0, :, 0]) and np.array_equal(lse[0, :, i], li[0, :, 0])
+
+
+def pin_window_limits(lib):
+    """Window 1 keeps only the diagonal key (O = v, LSE = s q.k); a window at
+    least Skv long is plain causal attention."""
+    rng = np.random.default_rng(20)
+    q = rng_tensor(rng, (2, 2, 7, 8)); k = rng_tensor(rng, (2, 2, 10, 8)); v = rng_tensor(rng, (2, 2, 10, 8))
+    o, lse = oracle.attention(q, k, v, 0.5, True, window=1, lib=lib)
+    for i in range(7):
+        j = i + 3
+        assert np.array_equal(o[:, :, i], v[:, :, j].astype(np.float64))
+        want = 0.5 * np.einsum("bhd,bhd->bh", q[:, :, i].astype(np.float64), k[:, :, j].astype(np.float64))
+        assert np.abs(lse[:, :, i] - want).max() <= 1e-12
+    oc, lc = oracle.attention(q, k, v, 0.5, True, lib=lib)
+    ow, lw = oracle.attention(q, k, v, 0.5, True, window=10, lib=lib)
+    assert np.array_equal(oc, ow) and np.array_equal(lc, lw)
+    # a window implies the causal bound (the band ends at the diagonal)
+    on, ln = oracle.attention(q, k, v, 0.5, False, window=10, lib=lib)
+    assert np.array_equal(oc, on) and np.array_equal(lc, ln)
+
+
+def pin_sink_is_extra_key(lib):
+    """A sink is a key that every row sees, whose score is the sink and whose
+    value is zero: realised with an extra feature (q[.., d] = 1, key 0 =
+    (0, .., 0, sink), value 0) at scale 1, where the products are exact."""
+    rng = np.random.default_rng(21)
+    B, H, sq, skv, d = 2, 3, 6, 9, 8
+    q = rng_tensor(rng, (B, H, sq, d)); k = rng_tensor(rng, (B, H, skv, d)); v = rng_tensor(rng, (B, H, skv, d))
+    sinks = np.array([0.75, -2.5, 4.0])
+    for causal in (False, True):
+        o, lse = oracle.attention(q, k, v, 1.0, causal, sinks=sinks, lib=lib)
+        q2 = np.concatenate([q, np.ones((B, H, sq, 1), np.float32)], axis=-1)
+        k2 = np.zeros((B, H, skv + 1, d + 1), np.float32)
+        k2[:, :, 1:, :d] = k
+        k2[:, :, 0, d] = sinks[None, :].astype(np.float32)
+        v2 = np.zeros((B, H, skv + 1, d + 1), np.float32)
+        v2[:, :, 1:, :d] = v
+        o2, lse2 = oracle.attention(q2, k2, v2, 1.0, causal, lib=lib)
+        assert np.abs(o2[..., :d] - o).max() <= 1e-13 and np.abs(lse2 - lse).max() <= 1e-12
+
+
+def pin_sink_splits_the_normaliser(lib):
+    """With or without a window, the sink only adds exp(sink) to the
+    normaliser: LSE' = logaddexp(LSE, sink) and O' = O exp(LSE - LSE'); a
+    row with no key gets O' = 0, LSE' = sink; sink = -inf changes nothing;
+    a sink far above every score stays finite (the max-with-sink guard)."""
+    rng = np.random.default_rng(22)
+    q = rng_tensor(rng, (1, 2, 10, 8)); k = rng_tensor(rng, (1, 2, 6, 8)); v = rng_tensor(rng, (1, 2, 6, 8))
+    for window in (0, 3):
+        o, lse = oracle.attention(q, k, v, 0.5, True, window=window, lib=lib)
+        for sk in ([0.3, -1.0], [800.0, 900.0]):
+            sinks = np.array(sk)
+            o2, lse2 = oracle.attention(q, k, v, 0.5, True, window=window, sinks=sinks, lib=lib)
+            assert np.all(np.isfinite(o2)) and np.all(np.isfinite(lse2))
+            want = np.logaddexp(lse, sinks[None, :, None])
+            assert np.abs(lse2 - want).max() <= 1e-12
+            scale = np.where(np.isneginf(lse), 0.0, np.exp(lse - want))
+            assert np.abs(o2 - o * scale[..., None]).max() <= 1e-13
+        o3, lse3 = oracle.attention(q, k, v, 0.5, True, window=window, sinks=np.array([-np.inf, -np.inf]),
+                                    lib=lib)
+        assert np.array_equal(o3, o) and np.array_equal(lse3, lse)
+
+
 ALL_PINS = [pin_four_scores, pin_three_blocks, pin_sdpa, pin_closed_forms, pin_shift_invariance,
             pin_rows_sum_to_one, pin_gqa_is_repeated_mha, pin_causal_is_prefix, pin_varlen_is_dense,
-            pin_row_subset]
+            pin_row_subset, pin_window_is_key_slice, pin_window_limits, pin_sink_is_extra_key,
+            pin_sink_splits_the_normaliser]

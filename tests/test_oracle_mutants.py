@@ -18,12 +18,19 @@ MUTANTS = {
     "causal_strict": ("(int64_t)i + (skv - sq) + 1;", "(int64_t)i + (skv - sq);"),
     "causal_top_left": ("(int64_t)i + (skv - sq) + 1;", "(int64_t)i + 1;"),
     "gqa_modulo": ("int hk = h / group;", "int hk = h % J->Hkv;"),
-    "v_uses_k": ("const float* vrow = vbase + j * d;", "const float* vrow = kbase + j * d;"),
-    "last_key_dropped": ("for (int64_t j = 0; j < nvis; ++j) {\n        s[j] = exp",
-                         "for (int64_t j = 0; j + 1 < nvis; ++j) {\n        s[j] = exp"),
+    "v_uses_k": ("const float* vrow = vbase + (jlo + j) * d;", "const float* vrow = kbase + (jlo + j) * d;"),
+    "last_key_dropped": ("for (int64_t j = 0; j < n; ++j) {\n        s[j] = exp",
+                         "for (int64_t j = 0; j + 1 < n; ++j) {\n        s[j] = exp"),
     "empty_row_lse_zero": ("if (lout) *lout = -INFINITY;", "if (lout) *lout = 0.0;"),
     "tail_key_dropped": ("int64_t nvis = skv;", "int64_t nvis = skv - 1;"),
     "varlen_kv_offset": ("kbase = J->k + ((int64_t)hk * T + start) * d;", "kbase = J->k + ((int64_t)hk * T) * d;"),
+    "window_off_by_one": ("jlo = (int64_t)i + (skv - sq) - J->window + 1;", "jlo = (int64_t)i + (skv - sq) - J->window;"),
+    "window_not_causal": ("if (J->causal || J->window > 0) {", "if (J->causal) {"),
+    "window_from_top_left": ("jlo = (int64_t)i + (skv - sq) - J->window + 1;", "jlo = (int64_t)i - J->window + 1;"),
+    "sink_sign": ("if (J->sinks) l += exp(sink - m);", "if (J->sinks) l += exp(m - sink);"),
+    "sink_dropped": ("if (J->sinks) l += exp(sink - m);", ";"),
+    "sink_no_max": ("if (J->sinks && sink > m) m = sink;", ";"),
+    "sink_empty_row_lse": ("if (lout && J->sinks) *lout = sink;", ";"),
 }
 
 
