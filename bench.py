@@ -5,8 +5,9 @@ Sq=Skv=8192, d=128, bf16, non-causal), inputs resident in HBM.  The JSON line
 reports whole-job TFLOP/s (4*B*H*Sq*Skv*d flop per step), the prefill
 kernel's roofline (MFMA bf16 peak), the fp64 CPU oracle timed on a bounded
 sample of the same workload, and, under "workloads", the other shapes: the
-causal 8K run, the 2K d=64 causal run, varlen grouped-query prefill and
-split-KV decode over a contiguous and a paged cache (HBM roofline).
+causal 8K run, the 2K d=64 causal run, varlen grouped-query prefill,
+sliding-window attention with sinks at 32K tokens, and split-KV decode over
+a contiguous and a paged cache (HBM roofline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 """
@@ -105,6 +106,12 @@ def run_workload(name: str, steps: int, warmup: int, inputs=None):
         def step():
             ea.attn_fwd_paged(q, k, v, bt, sl, o, lse, scale=wl.scale, num_splits=ns, workspace=ws,
                               stream=stream.cuda_stream)
+    elif wl.window > 0 or wl.sinks:
+        sk = torch.from_numpy(x["sinks"]).cuda() if wl.sinks else None
+
+        def step():
+            ea.attn_fwd_window_sink(q, k, v, o, lse, window=wl.window, sinks=sk, scale=wl.scale, cu_seqlens=cu,
+                                    num_splits=ns, workspace=ws, stream=stream.cuda_stream)
     else:
         def step():
             ea.attn_fwd_ex(q, k, v, o, lse, causal=wl.causal, scale=wl.scale, cu_seqlens=cu, num_splits=ns,
@@ -208,7 +215,7 @@ def main(argv=None):
     workloads = {}
     if not args.quick:
         for name in ("mha_causal_s8192_d128", "mha_causal_s2048_d64", "varlen_gqa_causal_d128",
-                     "decode_gqa_s16384_d128", "decode_paged_gqa_s16384_d128"):
+                     "swa_sink_s32768_d128", "decode_gqa_s16384_d128", "decode_paged_gqa_s16384_d128"):
             print(f"# timing {name}", file=sys.stderr, flush=True)
             w, ns, tt = run_workload(name, args.steps, args.warmup)
             entry = {"ms_per_step": round(tt["wall_ms_per_step"], 4), "launch_ms_mean": round(tt["event_ms_mean"], 4)}

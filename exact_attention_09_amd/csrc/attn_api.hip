@@ -98,10 +98,15 @@ int attn_decode_num_splits(int B, int Hkv, int Skv) {
   return e > 0 ? e : heuristic_splits(B, Hkv, Skv);
 }
 
-attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                        int H, int Hkv, int Sq, int Skv, int d, float scale, int causal,
-                        const int32_t* cu_seqlens, void* stream, attn_dtype dtype,
-                        const attn_opts* opts) {
+}  // extern "C"
+
+namespace {
+
+// The forward pass behind attn_fwd_ex and attn_fwd_window_sink: window > 0
+// and sinks != NULL are the causal bf16 variants (validated by the caller).
+attn_status forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                    int Sq, int Skv, int d, float scale, int causal, const int32_t* cu_seqlens, void* stream,
+                    attn_dtype dtype, const attn_opts* opts, int window, const float* sinks) {
   g_err[0] = '\0';
   // ---- validation: no HIP call until every check has passed
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return fail(ATTN_EINVAL, "unknown dtype %d", (int)dtype);
@@ -137,8 +142,11 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  p.window = window;
+  p.sinks = sinks;
   hipStream_t st = (hipStream_t)stream;
   const bool bf16 = dtype == ATTN_BF16;
+  const bool local = window > 0 || sinks != nullptr;
 
   if (!varlen && Skv == 0) {
     const hipError_t e = attn::launch_fill_empty(p, bf16, st);
@@ -147,8 +155,9 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
 
   const bool decode = !varlen && Sq == 1;
   if (!decode) {
-    // ATTN_BASIC_PREFILL selects the basic tiled kernel instead
-    const bool pingpong = bf16 && getenv("ATTN_BASIC_PREFILL") == nullptr;
+    // ATTN_BASIC_PREFILL selects the basic tiled kernel instead (it has no
+    // window or sink)
+    const bool pingpong = bf16 && (local || getenv("ATTN_BASIC_PREFILL") == nullptr);
     const int bm = !bf16 ? attn::f32_block_m()
                          : (pingpong ? attn::prefill_pp_block_m() : attn::prefill_bf16_block_m());
     const long tiles = varlen ? (long)Sq / bm + B : attn::ceil_div(Sq, bm);
@@ -175,8 +184,9 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
   }
 
   // ---- split-KV decode
-  int splits = (opts != nullptr && opts->num_splits > 0) ? opts->num_splits : attn_decode_num_splits(B, Hkv, Skv);
-  if (splits > Skv) splits = Skv;  // keep every split non-empty when possible
+  const int keys = (window > 0 && window < Skv) ? window : Skv;  // keys the query sees
+  int splits = (opts != nullptr && opts->num_splits > 0) ? opts->num_splits : attn_decode_num_splits(B, Hkv, keys);
+  if (splits > keys) splits = keys;  // keep every split non-empty when possible
   if (splits < 1) splits = 1;
   p.num_splits = splits;
   p.split_len = attn::ceil_div(Skv, splits);
@@ -215,6 +225,28 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
     if (ef != hipSuccess && status == ATTN_OK) status = hip_fail(ef, "workspace release");
   }
   return status;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int Hkv, int Sq, int Skv, int d, float scale, int causal,
+                        const int32_t* cu_seqlens, void* stream, attn_dtype dtype,
+                        const attn_opts* opts) {
+  return forward(q, k, v, o, lse, B, H, Hkv, Sq, Skv, d, scale, causal, cu_seqlens, stream, dtype, opts, 0,
+                 nullptr);
+}
+
+attn_status attn_fwd_window_sink(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                 int Hkv, int Sq, int Skv, int d, float scale, const int32_t* cu_seqlens,
+                                 int window, const float* sinks, void* stream, const attn_opts* opts) {
+  g_err[0] = '\0';
+  if (window < 0) return fail(ATTN_EINVAL, "window %d < 0", window);
+  if (sinks != nullptr && !aligned(sinks, 4)) return fail(ATTN_EINVAL, "sinks must be 4-byte aligned");
+  return forward(q, k, v, o, lse, B, H, Hkv, Sq, Skv, d, scale, 1, cu_seqlens, stream, ATTN_BF16, opts, window,
+                 sinks);
 }
 
 attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

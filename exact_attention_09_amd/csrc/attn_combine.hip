@@ -15,6 +15,7 @@ namespace attn {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 
 template <typename OutT>
 __device__ inline OutT cast_out(float x);
@@ -39,11 +40,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const Params p) {
   const float* gl = p.ws_lse + row * S;
   const float* po = p.ws_o + row * S * D + lane * DPL;
 
+  // an attention sink (tutorial sections 4.6 and 4.7) is one more term of
+  // the denominator, with no value: it joins the max and the sum only
+  const float sink = p.sinks != nullptr ? p.sinks[row % p.H] * kLog2e : -INFINITY;
   float gmax = -INFINITY;
   for (int s0 = 0; s0 < S; s0 += 64)
     if (s0 + lane < S) gmax = fmaxf(gmax, gl[s0 + lane]);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) gmax = fmaxf(gmax, shfl_xor_f(gmax, m));
+  gmax = fmaxf(gmax, sink);
   OutT* orow = (OutT*)p.o + row * D + lane * DPL;
   if (gmax == -INFINITY) {
 #pragma unroll
@@ -56,6 +61,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const Params p) {
     if (s0 + lane < S) tot += fast_exp2(gl[s0 + lane] - gmax);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) tot += shfl_xor_f(tot, m);
+  if (sink > -INFINITY) tot += fast_exp2(sink - gmax);
   const float gtot = fast_log2(tot) + gmax;
 
   vec_t acc = {};
@@ -78,14 +84,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const Params p) {
   if (p.lse != nullptr && lane == 0) p.lse[row] = gtot * kLn2;
 }
 
+// Rows [head-major runs of `run` rows per head]: O = 0; LSE = -inf, or the
+// head's sink when sinks are given (the sink is then the only term of the
+// denominator).
 template <typename OutT>
-__global__ __launch_bounds__(256) void fill_empty_kernel(OutT* o, float* lse, long rows, int d) {
+__global__ __launch_bounds__(256) void fill_empty_kernel(OutT* o, float* lse, long rows, int d, const float* sinks,
+                                                         int H, int run) {
   const long n = rows * d;
   for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256)
     o[i] = cast_out<OutT>(0.0f);
   if (lse != nullptr)
     for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < rows; i += (long)gridDim.x * 256)
-      lse[i] = -INFINITY;
+      lse[i] = sinks != nullptr ? sinks[(i / run) % H] : -INFINITY;
 }
 
 }  // namespace
@@ -115,12 +125,14 @@ hipError_t launch_fill_empty(const Params& p, bool out_bf16, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   long blocks = (rows * p.d + 255) / 256;
   if (blocks > 4096) blocks = 4096;
+  // lse is [B, H, Sq] (varlen [H, T]): runs of Sq rows per head
+  const int run = p.Sq > 0 ? p.Sq : 1;
   if (out_bf16)
     hipLaunchKernelGGL(fill_empty_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       (__bf16*)p.o, p.lse, rows, p.d);
+                       (__bf16*)p.o, p.lse, rows, p.d, p.sinks, p.H, run);
   else
     hipLaunchKernelGGL(fill_empty_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       (float*)p.o, p.lse, rows, p.d);
+                       (float*)p.o, p.lse, rows, p.d, p.sinks, p.H, run);
   return hipGetLastError();
 }
 

@@ -29,6 +29,10 @@
 // and lengths are clamped into range, so a malformed table gives wrong
 // numbers, never an out-of-bounds access.  Nothing else changes: the
 // indirection decides where the bytes come from, not what is computed.
+//
+// Sliding window (tutorial section 5.2): the single query row is the last
+// position, so a window of W keys keeps keys Skv - W .. Skv - 1, and the
+// splits cut that range.  An attention sink enters in the combine kernel.
 #include "attn_common.h"
 #include "attn_internal.h"
 
@@ -66,14 +70,17 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16_kernel(const Params 
   const int kvh = w % p.Hkv;
   const int b = w / p.Hkv;
 
-  int skv = p.Skv, split_len = p.split_len;
+  int skv = p.Skv;
   if constexpr (PAGED) {
     const int cap = p.max_pages << p.page_shift;
     skv = p.seqlens_k[b];
     skv = skv < 0 ? 0 : (skv > cap ? cap : skv);
-    split_len = ceil_div(skv, S);
   }
-  const int lo = s * split_len;
+  // a sliding window of W keys leaves the last W (the query is the last
+  // position, so the band ends at the last key)
+  const int kv_begin = (p.window > 0 && skv > p.window) ? skv - p.window : 0;
+  const int split_len = ceil_div(skv - kv_begin, S);
+  const int lo = kv_begin + s * split_len;
   int hi = lo + split_len;
   hi = hi < skv ? hi : skv;
   const int nchunks = hi > lo ? ceil_div(hi - lo, 32) : 0;

@@ -43,6 +43,16 @@
 //     max(m, rowmax), O and l scaled by exp2((m_old - m_new) scale'), P~
 //     again.  P~ stays <= 2^8 as with the lazy rescale of the basic kernel,
 //     which instead compares the tile max with m every tile.
+//   * Sliding window (causal only; TileLang tutorial section 5.2, the CUDA
+//     course chapter 12, section 12.9.5): key j is visible to row i iff
+//     i + off - W < j <= i + off.  The workgroup loads only the tiles from
+//     the first key its top row sees, each wave computes only the tiles its
+//     rows see, and tiles crossing the lower edge are masked like the
+//     diagonal ones.  Rows whose first tiles are fully masked keep no
+//     reference max until they see a key (the section 5.1 (1) check_inf).
+//   * Attention sink (tutorial sections 4.6 and 4.7): in the epilogue the
+//     sink's exp2(sink log2(e) - m*) joins the denominator, with
+//     m* = max(m scale', sink log2(e)) so that a large sink cannot overflow.
 #include "attn_common.h"
 #include "attn_internal.h"
 
@@ -52,6 +62,7 @@ namespace {
 
 constexpr float kSumCap = 256.0f;  // 2^8: bound on a lane's share of a tile row sum
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 // sequences a varlen call may have for the persistent (listed) order
 constexpr int kMaxListedSeqs = 1024;
 
@@ -102,8 +113,11 @@ __device__ inline unsigned lds_u32(const void* p) {
   return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+// LOCAL: the sliding-window / sink variant (causal only); off, the kernel is
+// compiled without any of its code.
+template <int D, bool CAUSAL, bool VARLEN, bool LOCAL>
 __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
+  static_assert(CAUSAL || !LOCAL, "windows and sinks are causal");
   constexpr int BN = D == 128 ? 64 : 128;  // keys per tile: 16 + 16 MFMAs per matrix phase
   constexpr int NW = 8;
   constexpr int BM = 32 * NW;              // 256
@@ -137,7 +151,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   // and skv keys (causal offset off) whose rows start at q_row0 (queries)
   // and kv_row0 (keys) in the head-major layout
   auto work = [&](const int tile_a, const int sq_a, const int skv_a, const int off_a, const int64_t q_row0_a,
-                  const int64_t kv_row0_a) {
+                  const int64_t kv_row0_a, const float sink_l2) {
   // the arguments are wave-uniform; readfirstlane lets the compiler keep them
   // (and the load descriptors built from them) in scalar registers
   const int tile = __builtin_amdgcn_readfirstlane(tile_a);
@@ -167,24 +181,39 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     for (int c = 0; c < NDC; ++c) qf[c] = bf16x8{};
   }
 
-  // ---- key ranges: the workgroup loads nt tiles, this wave computes nw
+  // ---- key ranges.  Tiles are numbered from key 0; the workgroup loads
+  // tiles t_first .. nt-1 (relative tile u is absolute tile t_first + u) and
+  // this wave computes tiles w_first .. nw-1.
+  const int W = LOCAL ? p.window : 0;
   const int q_hi = q0 + BM < sq ? q0 + BM : sq;
   const int kv_end = CAUSAL ? causal_kv_end(q_hi, off, skv) : skv;
   const int nt = ceil_div(kv_end, BN);
-  int w_end = 0;
+  // first key visible to row i under a window: i + off - W + 1
+  auto win_lo = [&](const int i) {
+    const long b = (long)i + off - W + 1;
+    return b < 0 ? 0 : (b > skv ? skv : (int)b);
+  };
+  const int t_first = W > 0 ? (win_lo(q0) < kv_end ? win_lo(q0) : kv_end) / BN : 0;
+  const int ntl = nt > t_first ? nt - t_first : 0;
+  int w_end = 0, w_first = 0;
   if (qw0 < sq) {
     const int w_hi = qw0 + 32 < sq ? qw0 + 32 : sq;
     w_end = CAUSAL ? causal_kv_end(w_hi, off, skv) : skv;
+    if (W > 0) w_first = win_lo(qw0) / BN;
   }
   const int nw = ceil_div(w_end, BN);
-  // keys < lim are visible to this lane's row; kept as lim - 4hh so that the
-  // per-register key offset it is compared with stays wave-uniform
+  // relative tile u is computed by this wave
+  auto computes = [&](const int u) { return u >= 0 && t_first + u >= w_first && t_first + u < nw; };
+  // keys < lim (and >= lo under a window) are visible to this lane's row;
+  // kept as lim - 4hh and lo - 4hh so that the per-register key offset they
+  // are compared with stays wave-uniform
   int lim = skv;
   if (CAUSAL) {
     const int c_lim = qrow + off + 1;
     lim = c_lim < lim ? c_lim : lim;
   }
   const int lim_h = lim - 4 * hh;
+  const int lo_h = (W > 0 ? qrow + off - W + 1 : -(1 << 30)) - 4 * hh;
 
   // ---- HBM -> LDS in MFMA fragment order, no registers on the way (keys
   // past skv arrive as zeros).  K block j = (d/16) kbi + c (1 KB): lane L
@@ -198,7 +227,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   const int v_lane_g = (8 * hh + 4 * (vg >> 1) + ((lane & 7) >> 1)) * ROWB + (16 * (vg & 1) + 8 * (lane & 1)) * 2;
   const int wu = __builtin_amdgcn_readfirstlane(wave);
   auto load_tile = [&](int u) {
-    const int k0 = u * BN;
+    const int k0 = (t_first + u) * BN;
     const int nrows = skv - k0 < BN ? skv - k0 : BN;
     const unsigned st = lds_u32(smem) + (u % STAGES) * STAGE_B;
     if (wu < 4) {
@@ -235,11 +264,11 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
 
   // ---- prologue: tiles 0 and 1
   for (int u = 0; u < PF; ++u)
-    if (u < nt) load_tile(u);
+    if (u < ntl) load_tile(u);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  const int nslots = 2 * nt + 2;
+  const int nslots = 2 * ntl + 2;
   for (int slot = 0; slot < nslots; ++slot) {
     // Tile k+PF is fetched into the stage of tile k+PF-STAGES, whose last
     // read (its V, by group B) was in slot 2k-1: its V blocks by group B in
@@ -249,7 +278,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     // burst from all eight waves at once delays both phases: measured.)
     if (((slot & 1) == 1) == (wu < 4)) {
       const int k = slot >> 1;
-      if (k + PF < nt) load_tile(k + PF);
+      if (k + PF < ntl) load_tile(k + PF);
     }
 
     const int ls = slot - grp;  // this group's own slot index
@@ -259,8 +288,8 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
         // matrix phase: P~V of tile t-1, then S^T of tile t.  Operand
         // fragments are double buffered in registers: the LDS reads of step
         // i+1 are in flight while the MFMAs of step i run.
-        const bool do_pv = t >= 1 && t - 1 < nw;
-        const bool do_qk = t < nw;
+        const bool do_pv = computes(t - 1);
+        const bool do_qk = computes(t);
         // the matrix phase issues first on this SIMD; the other group's
         // vector work fills the issue slots the MFMAs leave free
         __builtin_amdgcn_s_setprio(ATTN_PP_PRIO);
@@ -332,16 +361,19 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
         }
         }
         __builtin_amdgcn_s_setprio(0);
-      } else if (t < nw) {
+      } else if (computes(t)) {
         // vector phase for tile t
-        const int k0 = t * BN;
-        const bool partial = (k0 + BN > skv) || (CAUSAL && (k0 + BN - 1 > qw0 + off));
+        const int k0 = (t_first + t) * BN;
+        const bool partial = (k0 + BN > skv) || (CAUSAL && (k0 + BN - 1 > qw0 + off)) ||
+                             (W > 0 && k0 < qw0 + 31 + off - W + 1);
         if (partial) {
 #pragma unroll
           for (int kbi = 0; kbi < NKB; ++kbi)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)  // key = k0 + 32kbi + 8(r/4) + 4hh + r%4
-              if (k0 + 32 * kbi + 8 * (r >> 2) + (r & 3) >= lim_h) s[kbi][r] = -INFINITY;
+            for (int r = 0; r < 16; ++r) {  // key = k0 + 32kbi + 8(r/4) + 4hh + r%4
+              const int kk = k0 + 32 * kbi + 8 * (r >> 2) + (r & 3);
+              if (kk >= lim_h || (LOCAL && kk < lo_h)) s[kbi][r] = -INFINITY;
+            }
         }
         // P~ against the current reference, S kept; this lane's share of the
         // row sum as four independent chains
@@ -391,7 +423,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
       // immediate: expcnt and lgkmcnt at their maxima, vmcnt in the low four
       // bits)
       const int k = slot >> 1;
-      const int newer = (nt - 1 < k + PF ? nt - 1 : k + PF) - (k + 1);
+      const int newer = (ntl - 1 < k + PF ? ntl - 1 : k + PF) - (k + 1);
       if (PF >= 3 && newer >= 2) {
         __builtin_amdgcn_s_waitcnt(0x0F78);
       } else if (newer >= 1) {
@@ -403,10 +435,20 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     __syncthreads();
   }
 
-  // ---- epilogue: O = acc / l (0 for rows that saw no key), LSE natural log
-  const float l = pair32_sum(l_part);
+  // ---- epilogue: O = acc / l (0 for rows that saw no key), LSE natural
+  // log.  With a sink, acc and l are first brought to the reference
+  // m* = max(m scale', sink) and the sink's term is added to l.
+  float l = pair32_sum(l_part);
+  float ref_l2 = m_used * sl2;  // log2 of the reference the sums are relative to
+  float o_mul = 1.0f;
+  if (LOCAL && sink_l2 > -INFINITY) {
+    const float ms = fmaxf(m_used == -INFINITY ? -INFINITY : ref_l2, sink_l2);
+    o_mul = m_used == -INFINITY ? 0.0f : fast_exp2(ref_l2 - ms);
+    l = l * o_mul + fast_exp2(sink_l2 - ms);
+    ref_l2 = ms;
+  }
   if (qrow < sq) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float inv = l > 0.0f ? o_mul / l : 0.0f;
     __bf16* orow = O + (int64_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -420,7 +462,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
         *(bf16x4*)(orow + 32 * db + 8 * rg + 4 * hh) = w;
       }
     if (p.lse != nullptr && hh == 0)
-      p.lse[q_row0 + qrow] = l > 0.0f ? (m_used * sl2 + fast_log2(l)) * kLn2 : -INFINITY;
+      p.lse[q_row0 + qrow] = l > 0.0f ? (ref_l2 + fast_log2(l)) * kLn2 : -INFINITY;
   }
   };
 
@@ -429,6 +471,10 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   // false, and skip == true marks an empty item.
   int a_tile = 0, a_sq = 0, a_skv = 0, a_off = 0;
   int64_t a_q0 = 0, a_kv0 = 0;
+  float a_sink = -INFINITY;  // sink of the item's query head, log2 units
+  auto sink_of = [&](const int h) {
+    return (LOCAL && p.sinks != nullptr) ? p.sinks[h] * kLog2e : -INFINITY;
+  };
   // dense item v: (b, h) major, query tiles of a head heaviest first under
   // a causal mask
   auto dense_item = [&](const int v) {
@@ -442,6 +488,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     a_off = p.Skv - p.Sq;
     a_q0 = (int64_t)bh * p.Sq;
     a_kv0 = ((int64_t)b * p.Hkv + h / p.group) * p.Skv;
+    a_sink = sink_of(h);
   };
   // bounds of varlen sequence bb, clamped into [0, T]
   auto seq_bounds = [&](const int bb, int& s0, int& s1) {
@@ -460,6 +507,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     a_off = 0;
     a_q0 = (int64_t)h * p.Sq + s0;
     a_kv0 = (int64_t)(h / p.group) * p.Sq + s0;
+    a_sink = sink_of(h);
   };
   // varlen item v: h major, then the concatenated tiles of the sequences,
   // last first under a causal mask; false for items past the last tile
@@ -594,23 +642,25 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   for (int r = 0;; ++r) {
     bool skip;
     if (!item(r, skip)) break;
-    if (!skip) work(a_tile, a_sq, a_skv, a_off, a_q0, a_kv0);
+    if (!skip) work(a_tile, a_sq, a_skv, a_off, a_q0, a_kv0, a_sink);
     __syncthreads();
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool LOCAL>
 hipError_t launch_one(const Params& p, hipStream_t st) {
   const int grid = p.persist_c > 0 ? 8 * p.persist_c : 8 * ceil_div(p.work_items, 8);
-  hipLaunchKernelGGL((prefill_pp_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((prefill_pp_kernel<D, CAUSAL, VARLEN, LOCAL>), dim3(grid), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const Params& p, hipStream_t st) {
   const bool var = p.cu != nullptr;
-  if (p.causal) return var ? launch_one<D, true, true>(p, st) : launch_one<D, true, false>(p, st);
-  return var ? launch_one<D, false, true>(p, st) : launch_one<D, false, false>(p, st);
+  if (p.causal && (p.window > 0 || p.sinks != nullptr))
+    return var ? launch_one<D, true, true, true>(p, st) : launch_one<D, true, false, true>(p, st);
+  if (p.causal) return var ? launch_one<D, true, true, false>(p, st) : launch_one<D, true, false, false>(p, st);
+  return var ? launch_one<D, false, true, false>(p, st) : launch_one<D, false, false, false>(p, st);
 }
 
 }  // namespace

@@ -39,6 +39,8 @@ class Workload:
     lengths: tuple = field(default=())   # varlen sequence lengths (then B = len)
     num_splits: int = 0      # decode path split count (0 = library heuristic)
     page_size: int = 0       # > 0: decode over a paged KV cache of Skv keys per sequence
+    window: int = 0          # > 0: causal sliding window of this many keys
+    sinks: bool = False      # per-head attention sinks (seeded inputs)
 
     @property
     def paged(self) -> bool:
@@ -83,7 +85,17 @@ class Workload:
     def cu_seqlens(self):
         return synth.cu_seqlens_from_lengths(self.lengths) if self.varlen else None
 
+    def visible_pairs(self) -> float:
+        """(query, key) pairs a causal (optionally windowed) dense head sees."""
+        off = self.Skv - self.Sq
+        i = np.arange(self.Sq, dtype=np.int64)
+        hi = np.minimum(self.Skv, i + off + 1)
+        lo = np.maximum(0, i + off - self.window + 1) if self.window > 0 else np.zeros_like(i)
+        return float(np.maximum(0, hi - lo).sum())
+
     def flops(self) -> float:
+        if self.window > 0 and not self.varlen:
+            return 4.0 * self.B * self.H * self.d * self.visible_pairs()
         if self.varlen:
             return float(sum(4.0 * self.H * L * L * self.d * 0.5 if self.causal else 4.0 * self.H * L * L * self.d
                              for L in self.lengths))
@@ -113,6 +125,8 @@ class Workload:
         k = synth.normal_tensor(base + synth.TENSOR_K, self.kv_shape(), self.dtype)
         v = synth.normal_tensor(base + synth.TENSOR_V, self.kv_shape(), self.dtype)
         out = {"q": q, "k": k, "v": v, "cu_seqlens": self.cu_seqlens()}
+        if self.sinks:
+            out["sinks"] = synth.normal_tensor(base + synth.TENSOR_SINKS, (self.H,), "f32") * np.float32(2.0)
         if self.paged:
             out["block_table"] = synth.page_table(base + synth.TENSOR_PAGES, self.B, self.max_pages,
                                                   self.num_pages)
@@ -151,6 +165,11 @@ WORKLOADS = {
                                        causal=True, lengths=VARLEN_LENGTHS),
     "decode_gqa_s16384_d128": Workload("decode_gqa_s16384_d128", 5, B=32, H=32, Hkv=8, Sq=1, Skv=16384, d=128,
                                        dtype="bf16", causal=False, num_splits=16),
+    # sliding-window attention with per-head sinks at long context: a window
+    # of 4096 keys (the CUDA course's section 12.9.5 example) over 32K tokens,
+    # grouped-query heads
+    "swa_sink_s32768_d128": Workload("swa_sink_s32768_d128", 7, B=1, H=32, Hkv=8, Sq=32768, Skv=32768, d=128,
+                                     dtype="bf16", causal=True, window=4096, sinks=True),
     # the same decode over a paged cache: 16-token pages (the CUDA course's
     # typical block size) scattered by a seeded permutation
     "decode_paged_gqa_s16384_d128": Workload("decode_paged_gqa_s16384_d128", 6, B=32, H=32, Hkv=8, Sq=1,

@@ -117,6 +117,27 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
                         const int32_t* cu_seqlens, void* stream, attn_dtype dtype,
                         const attn_opts* opts);
 
+/* Causal attention with a sliding window and/or attention sinks, bf16.
+ * Same arguments and layouts as attn_fwd (dense or varlen), always causal
+ * (bottom-right aligned), plus:
+ *   window : 0 for none, else W > 0 keeps key j for query i iff
+ *            i + (Skv - Sq) - W < j <= i + (Skv - Sq) (the tutorial's
+ *            section 5.2 band; the CUDA course chapter 12, section 12.9.5).
+ *            The kernels load and compute only the key tiles inside the band.
+ *   sinks  : NULL, or [H] fp32 device array, one logit per query head in the
+ *            units of the scaled scores.  A sink joins each row's softmax
+ *            denominator and contributes no value (tutorial sections 4.6 and
+ *            4.7): O_i = sum_j e^(S_ij - m) v_j / (sum_j e^(S_ij - m) +
+ *            e^(sink - m)), m = max(max_j S_ij, sink), and LSE includes the
+ *            sink.  A row that sees no key gets O = 0 and LSE = sink (-inf
+ *            without sinks).
+ * Sq == 1 (dense) takes the split-KV decode path: the splits cut the window
+ * and the combine adds the sink.  Errors as for attn_fwd_ex; window < 0 is
+ * ATTN_EINVAL. */
+attn_status attn_fwd_window_sink(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                 int Hkv, int Sq, int Skv, int d, float scale, const int32_t* cu_seqlens,
+                                 int window, const float* sinks, void* stream, const attn_opts* opts);
+
 /* Split-KV decode over a paged KV cache: one query row per head (Sq == 1),
  * bf16.  A paged cache changes where the key and value bytes live, not what
  * is computed (tutorial section 4.8 (2)): the cache is cut into pages of

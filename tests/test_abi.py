@@ -144,3 +144,27 @@ def test_paged_rejects_before_any_hip_call(lib, kw, status):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(B=0, q=None, kc=None, vc=None, o=None, bt=None, sl=None)])
 def test_paged_empty_problem_is_a_no_op(lib, kw):
     assert paged_call(lib, **kw) == ea.ATTN_OK
+
+
+def window_call(lib, *, q=P, k=P, v=P, o=Q2, lse=None, B=1, H=4, Hkv=2, Sq=8, Skv=8, d=128, scale=0.1, cu=None,
+                window=0, sinks=None, opts=None):
+    return lib.attn_fwd_window_sink(q, k, v, o, lse, B, H, Hkv, Sq, Skv, d, scale, cu, window, sinks, None,
+                                    ctypes.byref(opts) if opts is not None else None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=-1), ea.ATTN_EINVAL),
+    (dict(sinks=ctypes.c_void_p(0x600002)), ea.ATTN_EINVAL),
+    (dict(q=None), ea.ATTN_EINVAL),
+    (dict(d=96), ea.ATTN_EUNSUPPORTED),
+    (dict(H=5, Hkv=2), ea.ATTN_EINVAL),
+    (dict(scale=0.0), ea.ATTN_EINVAL),
+])
+def test_window_sink_rejects_before_any_hip_call(lib, kw, status):
+    assert window_call(lib, **kw) == status
+    assert ea.attn_last_error() != ""
+
+
+def test_window_sink_empty_problem_is_a_no_op(lib):
+    assert window_call(lib, B=0, window=16) == ea.ATTN_OK
+    assert window_call(lib, Sq=0, window=16, sinks=P) == ea.ATTN_OK

@@ -1,0 +1,191 @@
+"""GPU parity for causal attention with a sliding window and per-head
+attention sinks (attn_fwd_window_sink) against the fp64 oracle.
+
+Bars as for the other bf16 tests (see test_parity_gpu.check).  A row that
+sees no key has O = 0 and LSE = its sink (-inf without sinks).  A window at
+least as long as the keys, with sinks of -inf, changes no mask and no term,
+so it must give the plain causal result up to the rounding differences of a
+separately compiled kernel variant (one bf16 ulp of O, a few fp32 ulps of
+LSE).
+"""
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_attention_09_amd import synth
+from exact_attention_09_amd.workloads import host_f32, to_device
+from test_parity_gpu import check, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_09_amd as ea
+    ea.load_library()
+    return ea
+
+
+def sink_values(seed, H):
+    """Seeded sinks around the scale of the scores, one far above them."""
+    s = synth.normal_tensor(seed, (H,), "f32").astype(np.float64) * 2.0
+    s[0] = 40.0
+    return s.astype(np.float32)
+
+
+def run(q, k, v, window, sinks, cu=None, num_splits=0):
+    import exact_attention_09_amd as ea
+    qt, kt, vt = (to_device(x, "bf16") for x in (q, k, v))
+    st = torch.from_numpy(sinks).cuda() if sinks is not None else None
+    cut = torch.from_numpy(np.asarray(cu, np.int32)).cuda() if cu is not None else None
+    o, lse = ea.attn_fwd_window_sink(qt, kt, vt, window=window, sinks=st, cu_seqlens=cut, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+DENSE = [
+    # (B, H, Hkv, Sq, Skv, d, window, with_sinks)
+    (1, 4, 2, 300, 300, 128, 64, True),
+    (2, 4, 4, 257, 257, 64, 1, False),          # the diagonal only
+    (1, 2, 2, 500, 700, 128, 100, True),        # Sq < Skv (bottom right)
+    (1, 2, 2, 700, 400, 128, 50, True),         # Sq > Skv: 300 rows see nothing
+    (2, 8, 2, 1024, 1024, 128, 256, True),      # window = one query tile
+    (1, 4, 4, 600, 600, 64, 1000, True),        # window longer than the keys
+    (1, 4, 4, 300, 300, 128, 0, True),          # sinks only
+    (1, 4, 1, 512, 512, 128, 129, False),       # band edge inside a key tile
+    (1, 6, 3, 400, 400, 64, 77, True),
+    (1, 4, 4, 128, 0, 128, 16, True),           # no keys: LSE = sink
+]
+
+
+@pytest.mark.parametrize("case", DENSE, ids=lambda c: "-".join(map(str, c)))
+def test_window_sink_dense(case):
+    B, H, Hkv, Sq, Skv, d, w, with_sinks = case
+    say(f"window/sink case {case}")
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    q = synth.normal_tensor(seed * 10 + 0, (B, H, Sq, d), "bf16")
+    k = synth.normal_tensor(seed * 10 + 1, (B, Hkv, Skv, d), "bf16")
+    v = synth.normal_tensor(seed * 10 + 2, (B, Hkv, Skv, d), "bf16")
+    sinks = sink_values(seed * 10 + 5, H) if with_sinks else None
+    o, lse = run(q, k, v, w, sinks)
+    scale = 1.0 / math.sqrt(d)
+    o_ref, lse_ref = oracle.attention(host_f32(q, "bf16"), host_f32(k, "bf16"), host_f32(v, "bf16"), scale, True,
+                                      window=w, sinks=sinks)
+    check(o, lse, o_ref, lse_ref, "bf16", str(case))
+
+
+def test_window_sink_persistent_grid():
+    """256 query tiles of 256 rows (persistent grid on a 256-CU part), GQA,
+    a window of 512 and sinks, against the oracle on sampled rows."""
+    B, H, Hkv, S, d, w = 1, 32, 8, 2048, 128, 512
+    say("window/sink persistent grid")
+    q = synth.normal_tensor(7300, (B, H, S, d), "bf16")
+    k = synth.normal_tensor(7301, (B, Hkv, S, d), "bf16")
+    v = synth.normal_tensor(7302, (B, Hkv, S, d), "bf16")
+    sinks = sink_values(7305, H)
+    o, lse = run(q, k, v, w, sinks)
+    rng = np.random.default_rng(7)
+    fixed = [0, 1, 255, 256, 511, 512, 513, 1023, 2047]
+    rows = [(0, int(rng.integers(H)), i) for i in fixed]
+    rows += [(0, int(rng.integers(H)), int(rng.integers(S))) for _ in range(150)]
+    rows = np.array(rows, np.int64)
+    o_ref, lse_ref = oracle.attention(host_f32(q, "bf16"), host_f32(k, "bf16"), host_f32(v, "bf16"),
+                                      1.0 / math.sqrt(d), True, rows=rows, window=w, sinks=sinks)
+    og = np.stack([o[b, h, i] for b, h, i in rows])
+    lg = np.array([lse[b, h, i] for b, h, i in rows])
+    check(og, lg, o_ref, lse_ref, "bf16", "persistent window/sink")
+
+
+@pytest.mark.parametrize("w,with_sinks", [(100, True), (1, False), (0, True)])
+def test_window_sink_varlen(w, with_sinks):
+    lengths = (5, 0, 1, 127, 300, 1000)
+    H, Hkv, d = 4, 2, 128
+    say(f"window/sink varlen w={w} sinks={with_sinks}")
+    T = sum(lengths)
+    cu = synth.cu_seqlens_from_lengths(lengths)
+    q = synth.normal_tensor(7400, (1, H, T, d), "bf16")
+    k = synth.normal_tensor(7401, (1, Hkv, T, d), "bf16")
+    v = synth.normal_tensor(7402, (1, Hkv, T, d), "bf16")
+    sinks = sink_values(7405, H) if with_sinks else None
+    o, lse = run(q, k, v, w, sinks, cu=cu)
+    o_ref, lse_ref = oracle.attention(host_f32(q, "bf16")[0], host_f32(k, "bf16")[0], host_f32(v, "bf16")[0],
+                                      1.0 / math.sqrt(d), True, cu_seqlens=cu, window=w, sinks=sinks)
+    check(o[0], lse[0], o_ref, lse_ref, "bf16", f"varlen w={w}")
+
+
+DECODE = [
+    # (B, H, Hkv, Skv, d, window, with_sinks, num_splits)
+    (3, 8, 2, 1000, 128, 300, True, 0),
+    (3, 8, 2, 1000, 128, 300, True, 16),
+    (2, 4, 4, 200, 64, 500, True, 4),       # window longer than the cache
+    (2, 40, 2, 700, 128, 64, False, 7),
+    (1, 4, 2, 0, 128, 10, True, 0),         # empty cache: LSE = sink
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "-".join(map(str, c)))
+def test_window_sink_decode(case):
+    B, H, Hkv, Skv, d, w, with_sinks, ns = case
+    say(f"window/sink decode {case}")
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    q = synth.normal_tensor(seed * 10 + 0, (B, H, 1, d), "bf16")
+    k = synth.normal_tensor(seed * 10 + 1, (B, Hkv, Skv, d), "bf16")
+    v = synth.normal_tensor(seed * 10 + 2, (B, Hkv, Skv, d), "bf16")
+    sinks = sink_values(seed * 10 + 5, H) if with_sinks else None
+    o, lse = run(q, k, v, w, sinks, num_splits=ns)
+    o_ref, lse_ref = oracle.attention(host_f32(q, "bf16"), host_f32(k, "bf16"), host_f32(v, "bf16"),
+                                      1.0 / math.sqrt(d), True, window=w, sinks=sinks)
+    check(o, lse, o_ref, lse_ref, "bf16", str(case))
+
+
+@pytest.mark.parametrize("Sq", [1, 700])
+def test_neutral_window_and_sinks_are_causal(Sq):
+    """A window covering every key and sinks of -inf change no mask and no
+    term: the plain causal forward, up to one bf16 ulp of O (the window and
+    sink variant is a separately compiled kernel, whose float contractions
+    may differ) and a few fp32 ulps of LSE."""
+    import exact_attention_09_amd as ea
+    say(f"neutral window/sinks Sq={Sq}")
+    H, Hkv, S, d = 8, 2, 900, 128
+    q = to_device(synth.normal_tensor(7500, (2, H, Sq, d), "bf16"), "bf16")
+    k = to_device(synth.normal_tensor(7501, (2, Hkv, S, d), "bf16"), "bf16")
+    v = to_device(synth.normal_tensor(7502, (2, Hkv, S, d), "bf16"), "bf16")
+    neg = torch.full((H,), -math.inf, dtype=torch.float32, device="cuda")
+    o1, l1 = ea.attn_fwd(q, k, v, causal=True)
+    o2, l2 = ea.attn_fwd_window_sink(q, k, v, window=S + Sq, sinks=neg)
+    torch.cuda.synchronize()
+    a, b = o1.float(), o2.float()
+    ulp = torch.clamp(a.abs(), min=2.0 ** -126)
+    ulp = torch.exp2(torch.floor(torch.log2(ulp)) - 7)
+    assert torch.all((a - b).abs() <= ulp), f"max |dO| {(a - b).abs().max().item():.3g}"
+    assert torch.all((l1 - l2).abs() <= 4e-7 * l1.abs() + 1e-7), f"max |dLSE| {(l1 - l2).abs().max().item():.3g}"
+
+
+def test_swa_workload_parity():
+    """The long-context window/sink workload at full size (32K tokens, window
+    4096, GQA) against the oracle on sampled rows, tile and band edges
+    included."""
+    from exact_attention_09_amd.workloads import WORKLOADS
+    wl = WORKLOADS["swa_sink_s32768_d128"]
+    say(f"workload {wl.name}: H={wl.H} Hkv={wl.Hkv} S={wl.Sq} d={wl.d} window={wl.window}")
+    x = wl.make_inputs()
+    o, lse = run(x["q"], x["k"], x["v"], wl.window, x["sinks"])
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(wl.wid)
+    fixed = [0, 1, 255, 256, 4095, 4096, 4097, 8191, 8192, 16384, 32766, 32767]
+    rows = [(0, int(rng.integers(wl.H)), i) for i in fixed]
+    rows += [(0, int(rng.integers(wl.H)), int(rng.integers(wl.Sq))) for _ in range(200)]
+    rows = np.array(rows, np.int64)
+    o_ref, lse_ref = oracle.attention(host_f32(x["q"], "bf16"), host_f32(x["k"], "bf16"), host_f32(x["v"], "bf16"),
+                                      wl.scale, True, rows=rows, window=wl.window, sinks=x["sinks"])
+    og = np.stack([o[b, h, i] for b, h, i in rows])
+    lg = np.array([lse[b, h, i] for b, h, i in rows])
+    check(og, lg, o_ref, lse_ref, "bf16", f"{wl.name} ({len(rows)} sampled rows)")
