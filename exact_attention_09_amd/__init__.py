@@ -13,6 +13,8 @@ Names mirror the C entry points:
   ``(o, lse)``;
 * ``attn_fwd_window_sink`` is causal attention with a sliding window and/or
   per-head attention sinks;
+* ``attn_fwd_layout`` is the general bf16 call: BHSD or BSHD (packed THD for
+  varlen) tensors, plus the window and sinks;
 * ``attn_fwd_paged`` runs split-KV decode over a paged KV cache (block
   table and per-sequence key counts) and returns ``(o, lse)``;
 * ``attn_workspace_bytes``, ``attn_decode_num_splits``,
@@ -29,10 +31,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn09.s
 
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ENOMEM, ATTN_EHIP = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
+ATTN_BHSD, ATTN_BSHD = 0, 1
 ATTN_MAX_SPLITS = 256
 
-EXPORTED = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_window_sink", "attn_fwd_paged",
-            "attn_workspace_bytes",
+EXPORTED = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_window_sink", "attn_fwd_layout",
+            "attn_fwd_paged", "attn_workspace_bytes",
             "attn_decode_num_splits", "attn_status_string", "attn_last_error")
 
 
@@ -70,6 +73,10 @@ def load_library(path: str = LIB_PATH):
     lib.attn_fwd_window_sink.restype = ctypes.c_int
     lib.attn_fwd_window_sink.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
         ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(AttnOpts)]
+    lib.attn_fwd_layout.restype = ctypes.c_int
+    lib.attn_fwd_layout.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.POINTER(AttnOpts)]
     lib.attn_fwd_paged.restype = ctypes.c_int
     lib.attn_fwd_paged.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 7 + [
         ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(AttnOpts)]
@@ -205,6 +212,69 @@ def attn_fwd_window_sink(q, k, v, o=None, lse=None, *, window: int = 0, sinks=No
     st = lib.attn_fwd_window_sink(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Sq, Skv, d,
                                   float(scale), _ptr(cu_seqlens), int(window), _ptr(sinks),
                                   ctypes.c_void_p(stream), ctypes.byref(opts))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_last_error())
+    return o, lse
+
+
+def attn_fwd_layout(q, k, v, o=None, lse=None, *, layout: str = "bshd", causal: bool = False, window: int = 0,
+                    sinks=None, scale: float | None = None, cu_seqlens=None, stream=None, num_splits: int = 0,
+                    workspace=None, want_lse: bool = True):
+    """bf16 forward through ``attn_fwd_layout``.
+
+    ``layout="bshd"``: q [B,Sq,H,d], k/v [B,Skv,Hkv,d]; with ``cu_seqlens``
+    the packed-token form q [T,H,d], k/v [T,Hkv,d].  ``layout="bhsd"``: the
+    shapes of ``attn_fwd_ex``.  lse is [B,H,Sq] ([H,T] varlen) either way.
+    ``window``/``sinks`` as for ``attn_fwd_window_sink`` (need ``causal``).
+    Returns ``(o, lse)``.
+    """
+    import torch
+    lib = load_library()
+    lay = {"bhsd": ATTN_BHSD, "bshd": ATTN_BSHD}[layout]
+    if lay == ATTN_BSHD:
+        if cu_seqlens is not None:
+            if q.dim() != 3 or k.dim() != 3:
+                raise ValueError("packed varlen tensors are [T, H, d]")
+            T, H, d = q.shape
+            Tk, Hkv, dk = k.shape
+            if Tk != T:
+                raise ValueError("varlen q and k must hold the same tokens")
+            B, Sq, Skv = cu_seqlens.numel() - 1, T, T
+            lse_shape = (H, T)
+        else:
+            if q.dim() != 4 or k.dim() != 4:
+                raise ValueError("BSHD tensors are [B, S, H, d]")
+            B, Sq, H, d = q.shape
+            Bk, Skv, Hkv, dk = k.shape
+            if Bk != B:
+                raise ValueError("q and k batch sizes differ")
+            lse_shape = (B, H, Sq)
+    else:
+        B, H, Hkv, Sq, Skv, d, dk = _shapes(q, k, cu_seqlens)
+        lse_shape = q.shape[:-1]
+    if dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must have the same shape, with q's d")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor on the GPU")
+    if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != H or not sinks.is_cuda
+                              or not sinks.is_contiguous()):
+        raise ValueError("sinks must be a contiguous float32 tensor of H values on the GPU")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise ValueError("cu_seqlens must be an int32 tensor on the GPU")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    opts = AttnOpts(int(num_splits), workspace.data_ptr() if workspace is not None else None,
+                    workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    st = lib.attn_fwd_layout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Sq, Skv, d, float(scale),
+                             int(bool(causal)), _ptr(cu_seqlens), lay, int(window), _ptr(sinks),
+                             ctypes.c_void_p(stream), ctypes.byref(opts))
     if st != ATTN_OK:
         raise AttnError(st, attn_last_error())
     return o, lse

@@ -106,10 +106,14 @@ namespace {
 // and sinks != NULL are the causal bf16 variants (validated by the caller).
 attn_status forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
                     int Sq, int Skv, int d, float scale, int causal, const int32_t* cu_seqlens, void* stream,
-                    attn_dtype dtype, const attn_opts* opts, int window, const float* sinks) {
+                    attn_dtype dtype, const attn_opts* opts, int window, const float* sinks,
+                    attn_layout layout) {
   g_err[0] = '\0';
   // ---- validation: no HIP call until every check has passed
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return fail(ATTN_EINVAL, "unknown dtype %d", (int)dtype);
+  if (layout != ATTN_BHSD && layout != ATTN_BSHD) return fail(ATTN_EINVAL, "unknown layout %d", (int)layout);
+  if (layout == ATTN_BSHD && dtype != ATTN_BF16)
+    return fail(ATTN_EUNSUPPORTED, "the BSHD layout is built for bf16 only");
   if (B < 0 || H < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || d < 0)
     return fail(ATTN_EINVAL, "negative size (B=%d H=%d Hkv=%d Sq=%d Skv=%d d=%d)", B, H, Hkv, Sq, Skv, d);
   if (opts != nullptr && (opts->num_splits < 0 || opts->num_splits > ATTN_MAX_SPLITS))
@@ -134,6 +138,7 @@ attn_status forward(const void* q, const void* k, const void* v, void* o, float*
   const long double q_elems = (long double)(varlen ? 1 : B) * H * Sq * d;
   const long double kv_elems = (long double)(varlen ? 1 : B) * Hkv * Skv * d;
   if (q_elems > 9.0e18L || kv_elems > 9.0e18L) return fail(ATTN_EINVAL, "tensor too large");
+  if ((long)H * d > 0x3fffffffL) return fail(ATTN_EINVAL, "H * d too large");
 
   attn::Params p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.cu = cu_seqlens;
@@ -144,6 +149,9 @@ attn_status forward(const void* q, const void* k, const void* v, void* o, float*
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.window = window;
   p.sinks = sinks;
+  p.bshd = layout == ATTN_BSHD ? 1 : 0;
+  p.q_rs = p.bshd ? H * d : d;
+  p.kv_rs = p.bshd ? Hkv * d : d;
   hipStream_t st = (hipStream_t)stream;
   const bool bf16 = dtype == ATTN_BF16;
   const bool local = window > 0 || sinks != nullptr;
@@ -157,7 +165,7 @@ attn_status forward(const void* q, const void* k, const void* v, void* o, float*
   if (!decode) {
     // ATTN_BASIC_PREFILL selects the basic tiled kernel instead (it has no
     // window or sink)
-    const bool pingpong = bf16 && (local || getenv("ATTN_BASIC_PREFILL") == nullptr);
+    const bool pingpong = bf16 && (local || p.bshd || getenv("ATTN_BASIC_PREFILL") == nullptr);
     const int bm = !bf16 ? attn::f32_block_m()
                          : (pingpong ? attn::prefill_pp_block_m() : attn::prefill_bf16_block_m());
     const long tiles = varlen ? (long)Sq / bm + B : attn::ceil_div(Sq, bm);
@@ -236,7 +244,7 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
                         const int32_t* cu_seqlens, void* stream, attn_dtype dtype,
                         const attn_opts* opts) {
   return forward(q, k, v, o, lse, B, H, Hkv, Sq, Skv, d, scale, causal, cu_seqlens, stream, dtype, opts, 0,
-                 nullptr);
+                 nullptr, ATTN_BHSD);
 }
 
 attn_status attn_fwd_window_sink(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -246,7 +254,20 @@ attn_status attn_fwd_window_sink(const void* q, const void* k, const void* v, vo
   if (window < 0) return fail(ATTN_EINVAL, "window %d < 0", window);
   if (sinks != nullptr && !aligned(sinks, 4)) return fail(ATTN_EINVAL, "sinks must be 4-byte aligned");
   return forward(q, k, v, o, lse, B, H, Hkv, Sq, Skv, d, scale, 1, cu_seqlens, stream, ATTN_BF16, opts, window,
-                 sinks);
+                 sinks, ATTN_BHSD);
+}
+
+attn_status attn_fwd_layout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                            int Sq, int Skv, int d, float scale, int causal, const int32_t* cu_seqlens,
+                            attn_layout layout, int window, const float* sinks, void* stream,
+                            const attn_opts* opts) {
+  g_err[0] = '\0';
+  if (window < 0) return fail(ATTN_EINVAL, "window %d < 0", window);
+  if ((window > 0 || sinks != nullptr) && !causal)
+    return fail(ATTN_EINVAL, "a window or sinks need causal attention");
+  if (sinks != nullptr && !aligned(sinks, 4)) return fail(ATTN_EINVAL, "sinks must be 4-byte aligned");
+  return forward(q, k, v, o, lse, B, H, Hkv, Sq, Skv, d, scale, causal, cu_seqlens, stream, ATTN_BF16, opts,
+                 window, sinks, layout);
 }
 
 attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
@@ -287,6 +308,8 @@ attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cac
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.block_table = block_table;
   p.seqlens_k = seqlens_k;
+  p.q_rs = d;
+  p.kv_rs = d;
   int shift = 0;
   while ((1 << shift) < page_size) ++shift;
   p.page_shift = shift;

@@ -36,6 +36,10 @@ struct Params {
   int page_shift;              // log2(page_size)
   int max_pages;               // row length of block_table
   int num_pages;               // pages in the cache (table entries are clamped into range)
+  // layout: row strides (elements) of q/o and k/v; bshd selects the
+  // [B, S, H, d] (varlen [T, H, d]) offsets instead of [B, H, S, d]
+  int q_rs, kv_rs;
+  int bshd;
   // sliding window and attention sinks (causal paths only)
   int window;                  // > 0: keys j with i + off - window < j <= i + off
   const float* sinks;          // [H] per-head sink logits (scaled-score units), or null

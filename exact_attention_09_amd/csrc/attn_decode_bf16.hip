@@ -90,9 +90,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16_kernel(const Params 
   const int h = kvh * p.group + (qvalid ? hl : 0);
 
   const __bf16* __restrict__ Q = (const __bf16*)p.q + ((int64_t)b * p.H + h) * D;
-  const int64_t kv0 = PAGED ? 0 : ((int64_t)b * p.Hkv + kvh) * p.Skv;
-  const __bf16* __restrict__ K = (const __bf16*)p.k + kv0 * D;
-  const __bf16* __restrict__ V = (const __bf16*)p.v + kv0 * D;
+  // element offset of key 0 of this (b, KV head) and the row stride: BHSD
+  // [B, Hkv, Skv, d] or BSHD [B, Skv, Hkv, d] (the query and output rows of
+  // a decode step are laid out alike in both)
+  int64_t kv0 = 0;
+  if constexpr (!PAGED) {
+    kv0 = p.bshd ? ((int64_t)b * p.Skv * p.Hkv + kvh) * D : ((int64_t)b * p.Hkv + kvh) * p.Skv * D;
+  }
+  const int kv_rs = PAGED ? D : p.kv_rs;
+  const __bf16* __restrict__ K = (const __bf16*)p.k + kv0;
+  const __bf16* __restrict__ V = (const __bf16*)p.v + kv0;
   const int32_t* __restrict__ table = PAGED ? p.block_table + (int64_t)b * p.max_pages : nullptr;
   // row of key `key` (< skv) relative to K and V
   auto key_row = [&](const int key) -> int64_t {
@@ -122,8 +129,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16_kernel(const Params 
       const int64_t row = key_row(key);
 #pragma unroll
       for (int c = 0; c < NDC; ++c) {
-        kr[kb][c] = *(const u32x4*)(K + row * D + 32 * c + 8 * kg);
-        vr[kb][c] = *(const u32x4*)(V + row * D + 32 * c + 8 * kg);
+        kr[kb][c] = *(const u32x4*)(K + row * kv_rs + 32 * c + 8 * kg);
+        vr[kb][c] = *(const u32x4*)(V + row * kv_rs + 32 * c + 8 * kg);
       }
     }
   };

@@ -114,8 +114,11 @@ __device__ inline unsigned lds_u32(const void* p) {
 }
 
 // LOCAL: the sliding-window / sink variant (causal only); off, the kernel is
-// compiled without any of its code.
-template <int D, bool CAUSAL, bool VARLEN, bool LOCAL>
+// compiled without any of its code.  BSHD: [B, S, H, d] tensors (row
+// strides H d and Hkv d, known at run time); off, rows are d apart and every
+// stride is a compile-time constant, as the address arithmetic of the
+// loaders is cheapest that way.
+template <int D, bool CAUSAL, bool VARLEN, bool LOCAL, bool BSHD>
 __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   static_assert(CAUSAL || !LOCAL, "windows and sinks are causal");
   constexpr int BN = D == 128 ? 64 : 128;  // keys per tile: 16 + 16 MFMAs per matrix phase
@@ -148,22 +151,28 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   const float sl2 = p.scale_log2;
 
   // ---- one work item: query tile `tile` of a sequence of sq query rows
-  // and skv keys (causal offset off) whose rows start at q_row0 (queries)
-  // and kv_row0 (keys) in the head-major layout
-  auto work = [&](const int tile_a, const int sq_a, const int skv_a, const int off_a, const int64_t q_row0_a,
-                  const int64_t kv_row0_a, const float sink_l2) {
+  // and skv keys (causal offset off).  Row 0 of its queries (and outputs)
+  // is element q_el of q (o), row 0 of its keys and values element kv_el of
+  // k and v; rows are p.q_rs and p.kv_rs elements apart.  Its LSE rows
+  // start at lse_row.
+  auto work = [&](const int tile_a, const int sq_a, const int skv_a, const int off_a, const int64_t q_el_a,
+                  const int64_t kv_el_a, const int64_t lse_row_a, const float sink_l2) {
   // the arguments are wave-uniform; readfirstlane lets the compiler keep them
   // (and the load descriptors built from them) in scalar registers
   const int tile = __builtin_amdgcn_readfirstlane(tile_a);
   const int sq = __builtin_amdgcn_readfirstlane(sq_a);
   const int skv = __builtin_amdgcn_readfirstlane(skv_a);
   const int off = __builtin_amdgcn_readfirstlane(off_a);
-  const int64_t q_row0 = uniform64(q_row0_a);
-  const int64_t kv_row0 = uniform64(kv_row0_a);
-  const __bf16* __restrict__ Q = (const __bf16*)p.q + q_row0 * D;
-  const __bf16* __restrict__ K = (const __bf16*)p.k + kv_row0 * D;
-  const __bf16* __restrict__ V = (const __bf16*)p.v + kv_row0 * D;
-  __bf16* __restrict__ O = (__bf16*)p.o + q_row0 * D;
+  const int64_t q_el = uniform64(q_el_a);
+  const int64_t kv_el = uniform64(kv_el_a);
+  const int64_t lse_row = uniform64(lse_row_a);
+  const int q_rs = BSHD ? __builtin_amdgcn_readfirstlane(p.q_rs) : D;
+  const int kv_rs = BSHD ? __builtin_amdgcn_readfirstlane(p.kv_rs) : D;
+  const int kv_rsb = 2 * kv_rs;  // bytes between key (value) rows
+  const __bf16* __restrict__ Q = (const __bf16*)p.q + q_el;
+  const __bf16* __restrict__ K = (const __bf16*)p.k + kv_el;
+  const __bf16* __restrict__ V = (const __bf16*)p.v + kv_el;
+  __bf16* __restrict__ O = (__bf16*)p.o + q_el;
 
   const int q0 = tile * BM;
   // the two waves on a SIMD take the two 32-row halves of one 64-row block,
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   bf16x8 qf[NDC];
   if (qrow < sq) {
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) qf[c] = *(const bf16x8*)(Q + (int64_t)qrow * D + 16 * c + 8 * hh);
+    for (int c = 0; c < NDC; ++c) qf[c] = *(const bf16x8*)(Q + (int64_t)qrow * q_rs + 16 * c + 8 * hh);
   } else {
 #pragma unroll
     for (int c = 0; c < NDC; ++c) qf[c] = bf16x8{};
@@ -222,27 +231,30 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   // V[16kc + 8e + 4(g>>1) + (L%8)/2][32db + 16(g&1) + 8(L%2) ..+8], g = (L%32)/8.
   // Waves 0-3 load the K blocks 4w .. 4w+3, waves 4-7 the V blocks
   // 4(w-4) .. +3: every wave reads whole 128-byte lines.
-  const int k_lane_g = l32 * ROWB + hh * 16;
+  const int k_lane_g = l32 * kv_rsb + hh * 16;
   const int vg = l32 >> 3;
-  const int v_lane_g = (8 * hh + 4 * (vg >> 1) + ((lane & 7) >> 1)) * ROWB + (16 * (vg & 1) + 8 * (lane & 1)) * 2;
+  const int v_lane_g = (8 * hh + 4 * (vg >> 1) + ((lane & 7) >> 1)) * kv_rsb + (16 * (vg & 1) + 8 * (lane & 1)) * 2;
   const int wu = __builtin_amdgcn_readfirstlane(wave);
   auto load_tile = [&](int u) {
     const int k0 = (t_first + u) * BN;
     const int nrows = skv - k0 < BN ? skv - k0 : BN;
+    // the descriptor ends right after row nrows-1: rows past it (and their
+    // neighbours' bytes in a strided layout) read as zeros
+    const int span = (nrows - 1) * kv_rsb + ROWB;
     const unsigned st = lds_u32(smem) + (u % STAGES) * STAGE_B;
     if (wu < 4) {
-      const __amdgpu_buffer_rsrc_t r = uniform_rsrc(K + (int64_t)k0 * D, nrows * ROWB);
+      const __amdgpu_buffer_rsrc_t r = uniform_rsrc(K + (int64_t)k0 * kv_rs, span);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 4 * wu + i, kbi = j / NDC, c = j % NDC;
-        load_lds16(r, k_lane_g, kbi * 32 * ROWB + c * 32, st + j * 1024);
+        load_lds16(r, k_lane_g, kbi * 32 * kv_rsb + c * 32, st + j * 1024);
       }
     } else {
-      const __amdgpu_buffer_rsrc_t r = uniform_rsrc(V + (int64_t)k0 * D, nrows * ROWB);
+      const __amdgpu_buffer_rsrc_t r = uniform_rsrc(V + (int64_t)k0 * kv_rs, span);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 4 * (wu - 4) + i, kc = j / NDB, db = j % NDB;
-        load_lds16(r, v_lane_g, kc * 16 * ROWB + db * 64, st + TILE_KV + j * 1024);
+        load_lds16(r, v_lane_g, kc * 16 * kv_rsb + db * 64, st + TILE_KV + j * 1024);
       }
     }
   };
@@ -449,7 +461,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   }
   if (qrow < sq) {
     const float inv = l > 0.0f ? o_mul / l : 0.0f;
-    __bf16* orow = O + (int64_t)qrow * D;
+    __bf16* orow = O + (int64_t)qrow * q_rs;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -462,15 +474,15 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
         *(bf16x4*)(orow + 32 * db + 8 * rg + 4 * hh) = w;
       }
     if (p.lse != nullptr && hh == 0)
-      p.lse[q_row0 + qrow] = l > 0.0f ? (ref_l2 + fast_log2(l)) * kLn2 : -INFINITY;
+      p.lse[lse_row + qrow] = l > 0.0f ? (ref_l2 + fast_log2(l)) * kLn2 : -INFINITY;
   }
   };
 
   // ---- scheduling.  Round r of this workgroup names one item through
-  // (tile, sq, skv, off, q_row0, kv_row0); the rounds end when item() returns
-  // false, and skip == true marks an empty item.
+  // (tile, sq, skv, off, q_el, kv_el, lse_row); the rounds end when item()
+  // returns false, and skip == true marks an empty item.
   int a_tile = 0, a_sq = 0, a_skv = 0, a_off = 0;
-  int64_t a_q0 = 0, a_kv0 = 0;
+  int64_t a_q0 = 0, a_kv0 = 0, a_lse0 = 0;
   float a_sink = -INFINITY;  // sink of the item's query head, log2 units
   auto sink_of = [&](const int h) {
     return (LOCAL && p.sinks != nullptr) ? p.sinks[h] * kLog2e : -INFINITY;
@@ -486,8 +498,15 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     a_sq = p.Sq;
     a_skv = p.Skv;
     a_off = p.Skv - p.Sq;
-    a_q0 = (int64_t)bh * p.Sq;
-    a_kv0 = ((int64_t)b * p.Hkv + h / p.group) * p.Skv;
+    const int kvh = h / p.group;
+    if constexpr (BSHD) {  // [B, S, H, d]
+      a_q0 = ((int64_t)b * p.Sq * p.H + h) * D;
+      a_kv0 = ((int64_t)b * p.Skv * p.Hkv + kvh) * D;
+    } else {       // [B, H, S, d]
+      a_q0 = (int64_t)bh * p.Sq * D;
+      a_kv0 = ((int64_t)b * p.Hkv + kvh) * p.Skv * D;
+    }
+    a_lse0 = (int64_t)bh * p.Sq;
     a_sink = sink_of(h);
   };
   // bounds of varlen sequence bb, clamped into [0, T]
@@ -505,8 +524,15 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     a_tile = tile;
     a_sq = a_skv = s1 - s0;
     a_off = 0;
-    a_q0 = (int64_t)h * p.Sq + s0;
-    a_kv0 = (int64_t)(h / p.group) * p.Sq + s0;
+    const int kvh = h / p.group;
+    if constexpr (BSHD) {  // [T, H, d]
+      a_q0 = ((int64_t)s0 * p.H + h) * D;
+      a_kv0 = ((int64_t)s0 * p.Hkv + kvh) * D;
+    } else {       // [1, H, T, d]
+      a_q0 = ((int64_t)h * p.Sq + s0) * D;
+      a_kv0 = ((int64_t)kvh * p.Sq + s0) * D;
+    }
+    a_lse0 = (int64_t)h * p.Sq + s0;
     a_sink = sink_of(h);
   };
   // varlen item v: h major, then the concatenated tiles of the sequences,
@@ -642,25 +668,31 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   for (int r = 0;; ++r) {
     bool skip;
     if (!item(r, skip)) break;
-    if (!skip) work(a_tile, a_sq, a_skv, a_off, a_q0, a_kv0, a_sink);
+    if (!skip) work(a_tile, a_sq, a_skv, a_off, a_q0, a_kv0, a_lse0, a_sink);
     __syncthreads();
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool LOCAL>
+template <int D, bool CAUSAL, bool VARLEN, bool LOCAL, bool BSHD>
 hipError_t launch_one(const Params& p, hipStream_t st) {
   const int grid = p.persist_c > 0 ? 8 * p.persist_c : 8 * ceil_div(p.work_items, 8);
-  hipLaunchKernelGGL((prefill_pp_kernel<D, CAUSAL, VARLEN, LOCAL>), dim3(grid), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((prefill_pp_kernel<D, CAUSAL, VARLEN, LOCAL, BSHD>), dim3(grid), dim3(512), 0, st, p);
   return hipGetLastError();
+}
+
+template <int D, bool BSHD>
+hipError_t launch_dl(const Params& p, hipStream_t st) {
+  const bool var = p.cu != nullptr;
+  if (p.causal && (p.window > 0 || p.sinks != nullptr))
+    return var ? launch_one<D, true, true, true, BSHD>(p, st) : launch_one<D, true, false, true, BSHD>(p, st);
+  if (p.causal)
+    return var ? launch_one<D, true, true, false, BSHD>(p, st) : launch_one<D, true, false, false, BSHD>(p, st);
+  return var ? launch_one<D, false, true, false, BSHD>(p, st) : launch_one<D, false, false, false, BSHD>(p, st);
 }
 
 template <int D>
 hipError_t launch_d(const Params& p, hipStream_t st) {
-  const bool var = p.cu != nullptr;
-  if (p.causal && (p.window > 0 || p.sinks != nullptr))
-    return var ? launch_one<D, true, true, true>(p, st) : launch_one<D, true, false, true>(p, st);
-  if (p.causal) return var ? launch_one<D, true, true, false>(p, st) : launch_one<D, true, false, false>(p, st);
-  return var ? launch_one<D, false, true, false>(p, st) : launch_one<D, false, false, false>(p, st);
+  return p.bshd ? launch_dl<D, true>(p, st) : launch_dl<D, false>(p, st);
 }
 
 }  // namespace

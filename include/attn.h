@@ -85,6 +85,14 @@ typedef enum {
 
 typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
 
+/* Tensor layouts (TileLang tutorial section 4.6: the two differ only in the
+ * index order; BSHD is how KV caches are usually stored).
+ *   ATTN_BHSD: q, o [B, H, Sq, d], k, v [B, Hkv, Skv, d]; varlen [1, H, T, d].
+ *   ATTN_BSHD: q, o [B, Sq, H, d], k, v [B, Skv, Hkv, d]; varlen (packed
+ *              tokens, "THD") [T, H, d] and [T, Hkv, d].
+ * lse is [B, H, Sq] (varlen [H, T]) in both. */
+typedef enum { ATTN_BHSD = 0, ATTN_BSHD = 1 } attn_layout;
+
 /* Largest split count the decode path accepts. */
 #define ATTN_MAX_SPLITS 256
 
@@ -137,6 +145,17 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
 attn_status attn_fwd_window_sink(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                  int Hkv, int Sq, int Skv, int d, float scale, const int32_t* cu_seqlens,
                                  int window, const float* sinks, void* stream, const attn_opts* opts);
+
+/* The general bf16 entry point: attn_fwd's arguments plus the tensor
+ * layout, a sliding window and sinks (as for attn_fwd_window_sink; window > 0
+ * or sinks != NULL need causal != 0, else ATTN_EINVAL).  attn_fwd,
+ * attn_fwd_ex (bf16) and attn_fwd_window_sink are this call with
+ * layout = ATTN_BHSD.  Errors as for attn_fwd_ex; an unknown layout is
+ * ATTN_EINVAL. */
+attn_status attn_fwd_layout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                            int Sq, int Skv, int d, float scale, int causal, const int32_t* cu_seqlens,
+                            attn_layout layout, int window, const float* sinks, void* stream,
+                            const attn_opts* opts);
 
 /* Split-KV decode over a paged KV cache: one query row per head (Sq == 1),
  * bf16.  A paged cache changes where the key and value bytes live, not what

@@ -168,3 +168,28 @@ def test_window_sink_rejects_before_any_hip_call(lib, kw, status):
 def test_window_sink_empty_problem_is_a_no_op(lib):
     assert window_call(lib, B=0, window=16) == ea.ATTN_OK
     assert window_call(lib, Sq=0, window=16, sinks=P) == ea.ATTN_OK
+
+
+def layout_call(lib, *, q=P, k=P, v=P, o=Q2, lse=None, B=1, H=4, Hkv=2, Sq=8, Skv=8, d=128, scale=0.1, causal=1,
+                cu=None, layout=1, window=0, sinks=None, opts=None):
+    return lib.attn_fwd_layout(q, k, v, o, lse, B, H, Hkv, Sq, Skv, d, scale, causal, cu, layout, window, sinks,
+                               None, ctypes.byref(opts) if opts is not None else None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=2), ea.ATTN_EINVAL),
+    (dict(layout=-1), ea.ATTN_EINVAL),
+    (dict(window=-2), ea.ATTN_EINVAL),
+    (dict(window=8, causal=0), ea.ATTN_EINVAL),
+    (dict(sinks=P, causal=0), ea.ATTN_EINVAL),
+    (dict(d=32), ea.ATTN_EUNSUPPORTED),
+    (dict(k=None), ea.ATTN_EINVAL),
+])
+def test_layout_rejects_before_any_hip_call(lib, kw, status):
+    assert layout_call(lib, **kw) == status
+    assert ea.attn_last_error() != ""
+
+
+def test_layout_empty_problem_is_a_no_op(lib):
+    assert layout_call(lib, B=0) == ea.ATTN_OK
+    assert layout_call(lib, Sq=0, window=4, sinks=P) == ea.ATTN_OK

@@ -1,0 +1,108 @@
+"""GPU parity for the BSHD layout (and packed THD for varlen) through
+attn_fwd_layout.  The layouts differ only in index order (tutorial section
+4.6), so the oracle is the BHSD oracle on transposed inputs, and the kernels,
+which run the same arithmetic on differently strided rows, must give bitwise
+the BHSD result.
+"""
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_attention_09_amd import synth
+from exact_attention_09_amd.workloads import host_f32, to_device
+from test_parity_gpu import check, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_09_amd as ea
+    ea.load_library()
+    return ea
+
+
+DENSE = [
+    # (B, H, Hkv, Sq, Skv, d, causal, window, with_sinks)
+    (2, 4, 2, 300, 300, 128, True, 0, False),
+    (1, 8, 8, 257, 257, 64, False, 0, False),
+    (2, 4, 1, 77, 200, 128, True, 0, False),
+    (1, 2, 2, 300, 130, 128, True, 0, False),    # Sq > Skv
+    (1, 6, 3, 500, 500, 64, True, 100, True),   # window and sinks
+    (3, 8, 2, 1, 1000, 128, False, 0, False),    # decode
+    (2, 8, 2, 1, 700, 128, True, 200, True),     # decode with window and sinks
+    (1, 32, 8, 2048, 2048, 128, True, 0, False), # persistent grid
+]
+
+
+def sinks_for(seed, H):
+    return (synth.normal_tensor(seed, (H,), "f32") * np.float32(2.0)).astype(np.float32)
+
+
+@pytest.mark.parametrize("case", DENSE, ids=lambda c: "-".join(map(str, c)))
+def test_bshd_dense(case):
+    import exact_attention_09_amd as ea
+    B, H, Hkv, Sq, Skv, d, causal, w, with_sinks = case
+    say(f"bshd case {case}")
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    q = synth.normal_tensor(seed * 10 + 0, (B, Sq, H, d), "bf16")
+    k = synth.normal_tensor(seed * 10 + 1, (B, Skv, Hkv, d), "bf16")
+    v = synth.normal_tensor(seed * 10 + 2, (B, Skv, Hkv, d), "bf16")
+    sinks = sinks_for(seed * 10 + 5, H) if with_sinks else None
+    st = torch.from_numpy(sinks).cuda() if sinks is not None else None
+    qt, kt, vt = (to_device(x, "bf16") for x in (q, k, v))
+    o, lse = ea.attn_fwd_layout(qt, kt, vt, layout="bshd", causal=causal, window=w, sinks=st)
+    # the same tensors in BHSD through the same general entry point
+    qh, kh, vh = (t.transpose(1, 2).contiguous() for t in (qt, kt, vt))
+    o2, lse2 = ea.attn_fwd_layout(qh, kh, vh, layout="bhsd", causal=causal, window=w, sinks=st)
+    torch.cuda.synchronize()
+    assert torch.equal(o.transpose(1, 2).contiguous().view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+    og = o.transpose(1, 2).float().cpu().numpy().astype(np.float64)
+    lg = lse.cpu().numpy().astype(np.float64)
+    tr = lambda x: np.ascontiguousarray(host_f32(x, "bf16").transpose(0, 2, 1, 3))
+    rows = None
+    if B * H * Sq > 20000:
+        rng = np.random.default_rng(seed)
+        rows = np.array([(int(rng.integers(B)), int(rng.integers(H)), i)
+                         for i in [0, 1, 255, 256, 1023, 1024, 2047] + list(rng.integers(0, Sq, 120))], np.int64)
+    o_ref, lse_ref = oracle.attention(tr(q), tr(k), tr(v), 1.0 / math.sqrt(d), causal, rows=rows, window=w,
+                                      sinks=sinks)
+    if rows is not None:
+        og = np.stack([og[b, h, i] for b, h, i in rows])
+        lg = np.array([lg[b, h, i] for b, h, i in rows])
+    check(og, lg, o_ref, lse_ref, "bf16", str(case))
+
+
+@pytest.mark.parametrize("causal,w", [(True, 0), (False, 0), (True, 64)])
+def test_thd_varlen(causal, w):
+    import exact_attention_09_amd as ea
+    lengths = (5, 0, 1, 127, 300, 1000, 257)
+    H, Hkv, d = 8, 2, 128
+    say(f"thd varlen causal={causal} window={w}")
+    T = sum(lengths)
+    cu = synth.cu_seqlens_from_lengths(lengths)
+    q = synth.normal_tensor(7600, (T, H, d), "bf16")
+    k = synth.normal_tensor(7601, (T, Hkv, d), "bf16")
+    v = synth.normal_tensor(7602, (T, Hkv, d), "bf16")
+    qt, kt, vt = (to_device(x, "bf16") for x in (q, k, v))
+    cut = torch.from_numpy(cu).cuda()
+    o, lse = ea.attn_fwd_layout(qt, kt, vt, layout="bshd", causal=causal, window=w,
+                                cu_seqlens=cut)
+    qh, kh, vh = (t.transpose(0, 1).contiguous().unsqueeze(0) for t in (qt, kt, vt))
+    o2, lse2 = ea.attn_fwd_layout(qh, kh, vh, layout="bhsd", causal=causal, window=w, cu_seqlens=cut)
+    torch.cuda.synchronize()
+    assert torch.equal(o.transpose(0, 1).contiguous().view(torch.int16), o2[0].view(torch.int16))
+    assert torch.equal(lse, lse2[0])
+    tr = lambda x: np.ascontiguousarray(host_f32(x, "bf16").transpose(1, 0, 2))
+    o_ref, lse_ref = oracle.attention(tr(q), tr(k), tr(v), 1.0 / math.sqrt(d), causal, cu_seqlens=cu, window=w)
+    og = o.transpose(0, 1).float().cpu().numpy().astype(np.float64)
+    check(og, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", f"thd causal={causal} w={w}")
