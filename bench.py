@@ -209,7 +209,7 @@ def main(argv=None):
                    "d": wl.d, "causal": wl.causal, "layout": "BHSD", "inputs": "N(0,1) seeded"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "prefill_pp_kernel<128,false,false>",
+                     "traffic": traffic, "kernel": "prefill_pp_kernel<128,false,false,false,false>",
                      "launch_ms_mean": round(t["event_ms_mean"], 4)},
     }
     workloads = {}
