@@ -6,8 +6,9 @@ reports whole-job TFLOP/s (4*B*H*Sq*Skv*d flop per step), the prefill
 kernel's roofline (MFMA bf16 peak), the fp64 CPU oracle timed on a bounded
 sample of the same workload, and, under "workloads", the other shapes: the
 causal 8K run, the 2K d=64 causal run, varlen grouped-query prefill,
-sliding-window attention with sinks at 32K tokens, and split-KV decode over
-a contiguous and a paged cache (HBM roofline).
+sliding-window attention with sinks at 32K tokens, split-KV decode over a
+contiguous and a paged cache (HBM roofline), and the backward pass of the
+8K shape (useful TFLOP/s, counted as 2.5 times the forward's).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 """
@@ -106,6 +107,15 @@ def run_workload(name: str, steps: int, warmup: int, inputs=None):
         def step():
             ea.attn_fwd_paged(q, k, v, bt, sl, o, lse, scale=wl.scale, num_splits=ns, workspace=ws,
                               stream=stream.cuda_stream)
+    elif wl.backward:
+        dout = to_device(x["dout"], wl.dtype)
+        ea.attn_fwd(q, k, v, o, lse, causal=wl.causal, scale=wl.scale)   # o, lse of the forward, untimed
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bws = torch.empty(ea.attn_bwd_workspace_bytes(wl.B, wl.H, wl.Sq), dtype=torch.uint8, device="cuda")
+
+        def step():
+            ea.attn_bwd(q, k, v, o, lse, dout, causal=wl.causal, scale=wl.scale, dq=dq, dk=dk, dv=dv,
+                        workspace=bws, stream=stream.cuda_stream)
     elif wl.window > 0 or wl.sinks:
         sk = torch.from_numpy(x["sinks"]).cuda() if wl.sinks else None
 
@@ -215,7 +225,8 @@ def main(argv=None):
     workloads = {}
     if not args.quick:
         for name in ("mha_causal_s8192_d128", "mha_causal_s2048_d64", "varlen_gqa_causal_d128",
-                     "swa_sink_s32768_d128", "decode_gqa_s16384_d128", "decode_paged_gqa_s16384_d128"):
+                     "swa_sink_s32768_d128", "decode_gqa_s16384_d128", "decode_paged_gqa_s16384_d128",
+                     "bwd_mha_s8192_d128", "bwd_mha_causal_s8192_d128"):
             print(f"# timing {name}", file=sys.stderr, flush=True)
             w, ns, tt = run_workload(name, args.steps, args.warmup)
             entry = {"ms_per_step": round(tt["wall_ms_per_step"], 4), "launch_ms_mean": round(tt["event_ms_mean"], 4)}

@@ -15,6 +15,7 @@ Names mirror the C entry points:
   per-head attention sinks;
 * ``attn_fwd_layout`` is the general bf16 call: BHSD or BSHD (packed THD for
   varlen) tensors, plus the window and sinks;
+* ``attn_bwd`` computes dq, dk, dv from the forward's o and lse;
 * ``attn_fwd_paged`` runs split-KV decode over a paged KV cache (block
   table and per-sequence key counts) and returns ``(o, lse)``;
 * ``attn_workspace_bytes``, ``attn_decode_num_splits``,
@@ -35,7 +36,7 @@ ATTN_BHSD, ATTN_BSHD = 0, 1
 ATTN_MAX_SPLITS = 256
 
 EXPORTED = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_window_sink", "attn_fwd_layout",
-            "attn_fwd_paged", "attn_workspace_bytes",
+            "attn_fwd_paged", "attn_bwd", "attn_bwd_workspace_bytes", "attn_workspace_bytes",
             "attn_decode_num_splits", "attn_status_string", "attn_last_error")
 
 
@@ -80,6 +81,11 @@ def load_library(path: str = LIB_PATH):
     lib.attn_fwd_paged.restype = ctypes.c_int
     lib.attn_fwd_paged.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 7 + [
         ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(AttnOpts)]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(AttnOpts)]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 3
     lib.attn_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_workspace_bytes.argtypes = [ctypes.c_int] * 4
     lib.attn_decode_num_splits.restype = ctypes.c_int
@@ -326,6 +332,43 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, o=None, lse=None
     if st != ATTN_OK:
         raise AttnError(st, attn_last_error())
     return o, lse
+
+
+def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = None, dq=None, dk=None,
+             dv=None, stream=None, workspace=None):
+    """Gradients through ``attn_bwd``: q [B,H,Sq,d], k/v [B,Hkv,Skv,d], the
+    forward's o and lse, and dout [B,H,Sq,d] (bf16 on the GPU).  Returns
+    ``(dq, dk, dv)``."""
+    import torch
+    lib = load_library()
+    B, H, Hkv, Sq, Skv, d, dk_ = _shapes(q, k, None)
+    if dk_ != d or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape) \
+            or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != tuple(q.shape[:-1]):
+        raise ValueError("shapes: q, o, dout [B,H,Sq,d]; k, v [B,Hkv,Skv,d]; lse [B,H,Sq]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor on the GPU")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 tensor on the GPU")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    opts = AttnOpts(0, workspace.data_ptr() if workspace is not None else None,
+                    workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                      B, H, Hkv, Sq, Skv, d, float(scale), int(bool(causal)), ctypes.c_void_p(stream),
+                      ctypes.byref(opts))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_last_error())
+    return dq, dk, dv
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, Sq: int) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, H, Sq))
 
 
 def attn_fwd(q, k, v, o=None, lse=None, **kw):

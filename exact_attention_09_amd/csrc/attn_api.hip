@@ -358,6 +358,86 @@ attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cac
   return status;
 }
 
+size_t attn_bwd_workspace_bytes(int B, int H, int Sq) {
+  if (B < 0 || H < 0 || Sq < 0) return 0;
+  return ((size_t)B * H * Sq * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, int B, int H, int Hkv, int Sq, int Skv, int d, float scale,
+                     int causal, void* stream, const attn_opts* opts) {
+  g_err[0] = '\0';
+  // ---- validation: no HIP call until every check has passed
+  if (B < 0 || H < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || d < 0)
+    return fail(ATTN_EINVAL, "negative size (B=%d H=%d Hkv=%d Sq=%d Skv=%d d=%d)", B, H, Hkv, Sq, Skv, d);
+  if (B == 0 || H == 0 || (Sq == 0 && Skv == 0)) return ATTN_OK;
+  if (Hkv < 1 || H % Hkv != 0) return fail(ATTN_EINVAL, "H=%d is not a multiple of Hkv=%d", H, Hkv);
+  if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "head dim %d (built: 64, 128)", d);
+  if (!(std::isfinite(scale) && scale > 0.0f))
+    return fail(ATTN_EINVAL, "scale must be finite and > 0 (got %g)", (double)scale);
+  if (Sq > 0 && (q == nullptr || o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr))
+    return fail(ATTN_EINVAL, "q, o, dout, lse and dq must not be NULL");
+  if (Skv > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return fail(ATTN_EINVAL, "k, v, dk and dv must not be NULL when Skv > 0");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(ATTN_EINVAL, "q, k, v, o, dout, dq, dk, dv must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(ATTN_EINVAL, "lse must be 4-byte aligned");
+  const long double q_elems = (long double)B * H * Sq * d;
+  const long double kv_elems = (long double)B * Hkv * Skv * d;
+  if (q_elems > 9.0e18L || kv_elems > 9.0e18L) return fail(ATTN_EINVAL, "tensor too large");
+  if ((long)B * H * attn::ceil_div(Sq, 128) > 0x7ffffff0L || (long)B * Hkv * attn::ceil_div(Skv, 128) > 0x7ffffff0L)
+    return fail(ATTN_EINVAL, "too many tiles");
+
+  attn::Params p{};
+  p.q = q; p.k = k; p.v = v; p.o = (void*)o; p.lse = (float*)lse;
+  p.B = B; p.H = H; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv; p.d = d;
+  p.group = H / Hkv;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  p.q_rs = d;
+  p.kv_rs = d;
+  hipStream_t st = (hipStream_t)stream;
+
+  if (Sq == 0) {
+    // no query: dK = dV = 0
+    attn::Params z = p;
+    z.B = 1; z.H = 1; z.Sq = (int)((long)B * Hkv * Skv); z.cu = nullptr; z.lse = nullptr; z.sinks = nullptr;
+    z.o = dk;
+    hipError_t e = attn::launch_fill_empty(z, true, st);
+    if (e == hipSuccess) {
+      z.o = dv;
+      e = attn::launch_fill_empty(z, true, st);
+    }
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "fill kernel");
+  }
+  const size_t need = attn_bwd_workspace_bytes(B, H, Sq);
+  void* ws = nullptr;
+  bool own = false;
+  if (opts != nullptr && opts->workspace != nullptr) {
+    if (opts->workspace_bytes < need)
+      return fail(ATTN_EINVAL, "workspace of %zu bytes, %zu needed", opts->workspace_bytes, need);
+    if (!aligned(opts->workspace, kWsAlign)) return fail(ATTN_EINVAL, "workspace must be 256-byte aligned");
+    ws = opts->workspace;
+  } else {
+    const hipError_t e = hipMallocAsync(&ws, need, st);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(ATTN_ENOMEM, "workspace of %zu bytes: %s", need, hipGetErrorString(e));
+    }
+    own = true;
+  }
+  attn_status status = ATTN_OK;
+  hipError_t e = attn::launch_backward(p, dout, (float*)ws, dq, dk, dv, st);
+  if (e != hipSuccess) status = hip_fail(e, "backward kernels");
+  if (own) {
+    const hipError_t ef = hipFreeAsync(ws, st);
+    if (ef != hipSuccess && status == ATTN_OK) status = hip_fail(ef, "workspace release");
+  }
+  return status;
+}
+
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int H, int Hkv, int Sq, int Skv, int d, float scale, int causal,
                      const int32_t* cu_seqlens, void* stream) {

@@ -18,7 +18,7 @@ Generator (counter based, so any slice can be produced independently):
   workloads, from fp32 to bf16 (round to nearest even on the fp32 bit pattern).
 
 Seeds: ``1000 * workload_id + tensor_id`` with tensor ids Q=0, K=1, V=2,
-sequence lengths=3, page tables=4, attention sinks=5 (N(0,1) times 2).
+sequence lengths=3, page tables=4, attention sinks=5 (N(0,1) times 2), output gradients=6.
 
 Page tables (paged KV caches): the physical pages are a seeded random
 permutation (the order of the stream outputs ``0 .. num_pages-1``, ties broken
@@ -37,7 +37,7 @@ GOLDEN_GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_LENGTHS, TENSOR_PAGES, TENSOR_SINKS = 0, 1, 2, 3, 4, 5
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_LENGTHS, TENSOR_PAGES, TENSOR_SINKS, TENSOR_DOUT = 0, 1, 2, 3, 4, 5, 6
 
 _CHUNK = 1 << 22  # normals per work item
 

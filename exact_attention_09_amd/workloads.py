@@ -17,6 +17,7 @@ Work counts (used for throughput, not by the computation):
 
 from __future__ import annotations
 
+import dataclasses
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -41,6 +42,7 @@ class Workload:
     page_size: int = 0       # > 0: decode over a paged KV cache of Skv keys per sequence
     window: int = 0          # > 0: causal sliding window of this many keys
     sinks: bool = False      # per-head attention sinks (seeded inputs)
+    backward: bool = False   # time the backward pass (dq, dk, dv) instead
 
     @property
     def paged(self) -> bool:
@@ -94,6 +96,10 @@ class Workload:
         return float(np.maximum(0, hi - lo).sum())
 
     def flops(self) -> float:
+        if self.backward:
+            # the usual count for the backward: five products of the forward's
+            # size (S recomputed, dP, dV, dQ, dK), 2.5 times the forward
+            return 2.5 * dataclasses.replace(self, backward=False).flops()
         if self.window > 0 and not self.varlen:
             return 4.0 * self.B * self.H * self.d * self.visible_pairs()
         if self.varlen:
@@ -127,6 +133,8 @@ class Workload:
         out = {"q": q, "k": k, "v": v, "cu_seqlens": self.cu_seqlens()}
         if self.sinks:
             out["sinks"] = synth.normal_tensor(base + synth.TENSOR_SINKS, (self.H,), "f32") * np.float32(2.0)
+        if self.backward:
+            out["dout"] = synth.normal_tensor(base + synth.TENSOR_DOUT, self.q_shape(), self.dtype)
         if self.paged:
             out["block_table"] = synth.page_table(base + synth.TENSOR_PAGES, self.B, self.max_pages,
                                                   self.num_pages)
@@ -170,6 +178,11 @@ WORKLOADS = {
     # grouped-query heads
     "swa_sink_s32768_d128": Workload("swa_sink_s32768_d128", 7, B=1, H=32, Hkv=8, Sq=32768, Skv=32768, d=128,
                                      dtype="bf16", causal=True, window=4096, sinks=True),
+    # the backward pass of the headline shape (dout seeded N(0, 1))
+    "bwd_mha_s8192_d128": Workload("bwd_mha_s8192_d128", 8, B=1, H=32, Hkv=32, Sq=8192, Skv=8192, d=128,
+                                   dtype="bf16", causal=False, backward=True),
+    "bwd_mha_causal_s8192_d128": Workload("bwd_mha_causal_s8192_d128", 9, B=1, H=32, Hkv=32, Sq=8192, Skv=8192,
+                                          d=128, dtype="bf16", causal=True, backward=True),
     # the same decode over a paged cache: 16-token pages (the CUDA course's
     # typical block size) scattered by a seeded permutation
     "decode_paged_gqa_s16384_d128": Workload("decode_paged_gqa_s16384_d128", 6, B=32, H=32, Hkv=8, Sq=1,

@@ -193,3 +193,34 @@ def test_layout_rejects_before_any_hip_call(lib, kw, status):
 def test_layout_empty_problem_is_a_no_op(lib):
     assert layout_call(lib, B=0) == ea.ATTN_OK
     assert layout_call(lib, Sq=0, window=4, sinks=P) == ea.ATTN_OK
+
+
+def bwd_call(lib, *, q=P, k=P, v=P, o=P, do=P, lse=P, dq=Q2, dk=Q2, dv=Q2, B=1, H=4, Hkv=2, Sq=8, Skv=8, d=128,
+             scale=0.1, causal=0, opts=None):
+    return lib.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, Hkv, Sq, Skv, d, scale, causal, None,
+                        ctypes.byref(opts) if opts is not None else None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ea.ATTN_EINVAL),
+    (dict(do=None), ea.ATTN_EINVAL),
+    (dict(lse=None), ea.ATTN_EINVAL),
+    (dict(dk=None), ea.ATTN_EINVAL),
+    (dict(H=6, Hkv=4), ea.ATTN_EINVAL),
+    (dict(d=96), ea.ATTN_EUNSUPPORTED),
+    (dict(scale=0.0), ea.ATTN_EINVAL),
+    (dict(dq=ctypes.c_void_p(0x200008)), ea.ATTN_EINVAL),
+    (dict(lse=ctypes.c_void_p(0x100002)), ea.ATTN_EINVAL),
+    (dict(Sq=-1), ea.ATTN_EINVAL),
+    (dict(opts=ea.AttnOpts(0, 0x500000, 16)), ea.ATTN_EINVAL),
+])
+def test_bwd_rejects_before_any_hip_call(lib, kw, status):
+    assert bwd_call(lib, **kw) == status
+    assert ea.attn_last_error() != ""
+
+
+def test_bwd_empty_and_workspace(lib):
+    assert bwd_call(lib, B=0) == ea.ATTN_OK
+    assert bwd_call(lib, Sq=0, Skv=0) == ea.ATTN_OK
+    assert ea.attn_bwd_workspace_bytes(2, 4, 100) == 3328  # 3200 bytes of Delta, rounded to 256
+    assert ea.attn_bwd_workspace_bytes(-1, 4, 100) == 0

@@ -1,0 +1,140 @@
+"""GPU parity for the backward pass (attn_bwd) against the fp64 backward
+oracle (``oracle/backward.py``) on the same bf16 inputs.
+
+The GPU side runs the real sequence: attn_fwd for o and lse, then attn_bwd.
+Bar (this library's reading; the pages print no backward tolerance): every
+element within 1e-2 of the largest magnitude of the exact gradient tensor,
+plus 1e-4 absolute for tensors that are exactly zero (a single visible key
+makes dq and dk vanish; the kernels then return rounding residue of about
+1e-6).
+The kernels round three things to bf16 -- the forward output o that Delta is
+formed from, the probabilities P and dS that feed the products, and the
+gradients they store -- each worth at most 2^-9 of a value, so a few parts in
+2^-8 of the tensor's scale is where a correct kernel lands; 1e-2 leaves a
+margin of about two.
+"""
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+
+from exact_attention_09_amd import synth
+from exact_attention_09_amd.workloads import WORKLOADS, host_f32, to_device
+from oracle import backward as bwd_oracle
+from test_parity_gpu import say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+REL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_09_amd as ea
+    ea.load_library()
+    return ea
+
+
+def run(q, k, v, do, causal):
+    import exact_attention_09_amd as ea
+    qt, kt, vt, dot = (to_device(x, "bf16") for x in (q, k, v, do))
+    o, lse = ea.attn_fwd(qt, kt, vt, causal=causal)
+    dq, dk, dv = ea.attn_bwd(qt, kt, vt, o, lse, dot, causal=causal)
+    torch.cuda.synchronize()
+    return tuple(x.float().cpu().numpy().astype(np.float64) for x in (dq, dk, dv))
+
+
+def compare(got, want, what):
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        assert np.all(np.isfinite(g)), f"{what}: non-finite {name}"
+        scale = max(np.abs(w).max(initial=0.0), 1e-30)
+        err = np.abs(g - w).max(initial=0.0)
+        say(f"  {what}: {name} max|err| {err:.3g} of max|{name}| {scale:.3g} ({err / scale:.2e})")
+        assert err <= REL * scale + 1e-4, f"{what}: {name} max|err| {err:.3g} > {REL} x {scale:.3g}"
+
+
+CASES = [
+    # (B, H, Hkv, Sq, Skv, d, causal)
+    (1, 2, 2, 128, 128, 64, False),
+    (2, 4, 2, 200, 200, 128, True),
+    (1, 4, 1, 77, 300, 128, True),     # Sq < Skv (bottom right), MQA
+    (1, 2, 2, 300, 130, 128, True),    # Sq > Skv: 170 rows see no key
+    (1, 8, 2, 512, 512, 128, False),   # GQA group 4
+    (1, 2, 2, 1, 100, 128, False),     # one query row
+    (1, 4, 4, 257, 1, 64, False),      # one key: dq = dk = 0
+    (2, 4, 4, 1000, 1000, 64, True),
+    (1, 6, 3, 333, 444, 64, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_backward_parity(case):
+    B, H, Hkv, Sq, Skv, d, causal = case
+    say(f"backward case {case}")
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    q = synth.normal_tensor(seed * 10 + 0, (B, H, Sq, d), "bf16")
+    k = synth.normal_tensor(seed * 10 + 1, (B, Hkv, Skv, d), "bf16")
+    v = synth.normal_tensor(seed * 10 + 2, (B, Hkv, Skv, d), "bf16")
+    do = synth.normal_tensor(seed * 10 + 3, (B, H, Sq, d), "bf16")
+    got = run(q, k, v, do, causal)
+    want = bwd_oracle.attention_backward(*(host_f32(x, "bf16") for x in (q, k, v, do)), 1.0 / math.sqrt(d), causal)
+    compare(got, want, str(case))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_long_sequence_two_heads(causal):
+    """4K tokens, 32 heads on the GPU; the oracle checks two of them (MHA, so
+    heads are independent)."""
+    B, H, S, d = 1, 32, 4096, 128
+    say(f"backward 4K causal={causal}")
+    q = synth.normal_tensor(8100, (B, H, S, d), "bf16")
+    k = synth.normal_tensor(8101, (B, H, S, d), "bf16")
+    v = synth.normal_tensor(8102, (B, H, S, d), "bf16")
+    do = synth.normal_tensor(8103, (B, H, S, d), "bf16")
+    got = run(q, k, v, do, causal)
+    heads = [0, 17]
+    want = bwd_oracle.attention_backward(*(host_f32(x, "bf16")[:, heads] for x in (q, k, v, do)),
+                                         1.0 / math.sqrt(d), causal)
+    compare(tuple(g[:, heads] for g in got), want, f"4K causal={causal} heads {heads}")
+
+
+def test_backward_no_keys_and_bitwise_repeatable():
+    import exact_attention_09_amd as ea
+    say("backward: no keys, repeatability")
+    q = to_device(synth.normal_tensor(8200, (1, 2, 64, 128), "bf16"), "bf16")
+    e = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    o, lse = ea.attn_fwd(q, e, e)
+    dq, dk, dv = ea.attn_bwd(q, e, e, o, lse, q)
+    torch.cuda.synchronize()
+    assert torch.all(dq.float() == 0.0)
+    k = to_device(synth.normal_tensor(8201, (2, 2, 700, 128), "bf16"), "bf16")
+    v = to_device(synth.normal_tensor(8202, (2, 2, 700, 128), "bf16"), "bf16")
+    q2 = to_device(synth.normal_tensor(8203, (2, 8, 600, 128), "bf16"), "bf16")
+    do = to_device(synth.normal_tensor(8204, (2, 8, 600, 128), "bf16"), "bf16")
+    o, lse = ea.attn_fwd(q2, k, v, causal=True)
+    r1 = ea.attn_bwd(q2, k, v, o, lse, do, causal=True)
+    r2 = ea.attn_bwd(q2, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.backward])
+def test_backward_workload(name):
+    """The timed backward workloads at their full size (32 heads of 8K
+    tokens, as timed); the oracle checks one head in full (MHA, so heads are
+    independent)."""
+    wl = WORKLOADS[name]
+    say(f"backward workload {name}")
+    x = wl.make_inputs()
+    got = run(x["q"], x["k"], x["v"], x["dout"], wl.causal)
+    heads = [wl.H - 3]
+    want = bwd_oracle.attention_backward(*(host_f32(x[n], wl.dtype)[:, heads] for n in ("q", "k", "v", "dout")),
+                                         wl.scale, wl.causal)
+    compare(tuple(g[:, heads] for g in got), want, f"{name} head {heads}")
