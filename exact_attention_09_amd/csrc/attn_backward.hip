@@ -142,10 +142,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf
   const int hh = lane >> 5;
   const float sl2 = p.scale_log2;
 
+  // causal: key tiles in order of decreasing work (a key tile's query range
+  // shrinks as the keys move right), so the light tiles fill the tail
   const int ktiles = ceil_div(p.Skv, BK);
   const int item = blockIdx.x;
-  const int kt = item % ktiles;
-  const int bk = item / ktiles;  // b * Hkv + kvh
+  const int nbk = p.B * p.Hkv;
+  const int kt = CAUSAL ? item / nbk : item % ktiles;
+  const int bk = CAUSAL ? item - kt * nbk : item / ktiles;  // b * Hkv + kvh
   const int b = bk / p.Hkv;
   const int kvh = bk - b * p.Hkv;
   const int sq = p.Sq, skv = p.Skv, off = skv - sq;
@@ -338,10 +341,13 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(const Params p, const __bf16
   const int hh = lane >> 5;
   const float sl2 = p.scale_log2;
 
+  // causal: query tiles in order of decreasing work (the last tiles see the
+  // most keys)
   const int qtiles = ceil_div(p.Sq, BMQ);
   const int item = blockIdx.x;
-  const int bh = item / qtiles;
-  const int tile = item - bh * qtiles;
+  const int nbh = p.B * p.H;
+  const int bh = CAUSAL ? item % nbh : item / qtiles;
+  const int tile = CAUSAL ? qtiles - 1 - item / nbh : item - bh * qtiles;
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int sq = p.Sq, skv = p.Skv, off = skv - sq;
