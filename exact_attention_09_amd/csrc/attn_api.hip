@@ -360,7 +360,8 @@ attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cac
 
 size_t attn_bwd_workspace_bytes(int B, int H, int Sq) {
   if (B < 0 || H < 0 || Sq < 0) return 0;
-  return ((size_t)B * H * Sq * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
+  // Delta and the log2-domain LSE, each rounded up to the alignment
+  return 2 * (((size_t)B * H * Sq * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign);
 }
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -429,7 +430,9 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
     own = true;
   }
   attn_status status = ATTN_OK;
-  hipError_t e = attn::launch_backward(p, dout, (float*)ws, dq, dk, dv, st);
+  float* delta = (float*)ws;
+  float* lse2 = (float*)((char*)ws + need / 2);
+  hipError_t e = attn::launch_backward(p, dout, delta, lse2, dq, dk, dv, st);
   if (e != hipSuccess) status = hip_fail(e, "backward kernels");
   if (own) {
     const hipError_t ef = hipFreeAsync(ws, st);

@@ -39,10 +39,13 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 // ---------------------------------------------------------------- Delta
 
-// Delta = rowsum(dO * O) per row, fp32; D/8 lanes per row, 16 bytes each.
+// Per row: Delta = rowsum(dO * O) in fp32, and the forward's LSE in log2
+// units for exp2, with +inf for a row that saw no key (LSE = -inf) so that
+// its P = exp2(s' - LSE') is 0.  D/8 lanes per row, 16 bytes each.
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                                                   float* __restrict__ delta, long rows) {
+                                                   const float* __restrict__ lse, float* __restrict__ delta,
+                                                   float* __restrict__ lse2, long rows) {
   constexpr int TPR = D / 8;
   constexpr int RPB = 256 / TPR;
   const int sub = threadIdx.x % TPR;
@@ -56,36 +59,31 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && sub == 0) delta[row] = acc;
+  if (row < rows && sub == 0) {
+    delta[row] = acc;
+    const float l = lse[row];
+    lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------- shared
 
-// Row-major tile of `rows` rows of D bf16 in LDS (16-byte chunks swizzled),
-// loaded through registers by 256 threads.
+// A row-major tile of `ROWS` rows of D bf16 in LDS, 16-byte chunks swizzled
+// (lds_off), filled straight from HBM by buffer_load ... lds.  The tile is a
+// run of 1 KB blocks; lane L of a block load writes bytes 16L .. 16L+15 of
+// the block, which is row L / (2D/16) of the block at chunk position
+// L % (2D/16), so the lane fetches the logical chunk that the swizzle puts
+// there.  `voff(j)` is that lane's byte offset in the HBM tile for block j.
 template <int D, int ROWS>
-struct TileLoader {
-  static constexpr int ROWB = D * 2;
-  static constexpr int CH = D / 8;
-  static constexpr int RPP = 256 / CH;
-  static constexpr int PASSES = ROWS / RPP;
-  static_assert(ROWS % RPP == 0, "tile rows must be a multiple of the load pass");
-  u32x4 reg[PASSES];
-  int c, r;
-  __device__ void init(int tid) {
-    c = tid % CH;
-    r = tid / CH;
-  }
-  // rows [0, valid) of `base` (row stride D); the rest read as zero
-  __device__ void load(const __bf16* base, int valid) {
-    const int n = valid < ROWS ? (valid > 0 ? valid : 0) : ROWS;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, n * ROWB);
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i) reg[i] = buffer_load16(rs, r * ROWB + c * 16, i * RPP * ROWB);
-  }
-  __device__ void store(unsigned char* lds) const {
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i) *(u32x4*)(lds + lds_off<D>(r + RPP * i, c)) = reg[i];
+struct SwizzledTile {
+  static constexpr int ROWB = 2 * D;
+  static constexpr int CPR = ROWB / 16;     // 16-byte chunks per row
+  static constexpr int RPB = 1024 / ROWB;   // rows per 1 KB block
+  static constexpr int NBLK = ROWS / RPB;   // blocks per tile
+  static constexpr int BYTES = ROWS * ROWB;
+  __device__ static int voff(int j, int lane) {
+    const int r = j * RPB + lane / CPR;
+    return r * ROWB + (((lane % CPR) ^ swz<D>(r)) << 4);
   }
 };
 
@@ -108,10 +106,9 @@ __device__ inline bf16x8 frag_cols(const unsigned char* tile, int kc, int db, in
   return join_tr(lo, hi);
 }
 
-// bf16 x 8 of accumulator registers 8(kc&1) .. +8 of block kc>>1
-__device__ inline bf16x8 chunk_bf16(const f32x16* acc, int kc) {
-  const f32x16& a = acc[kc >> 1];
-  const int rb = 8 * (kc & 1);
+// bf16 x 8 of accumulator registers 8h .. 8h+7
+__device__ inline bf16x8 half_bf16(const f32x16& a, int h) {
+  const int rb = 8 * h;
   return to_bf16x8(a[rb + 0], a[rb + 1], a[rb + 2], a[rb + 3], a[rb + 4], a[rb + 5], a[rb + 6], a[rb + 7]);
 }
 
@@ -120,24 +117,28 @@ __device__ inline bf16x8 chunk_bf16(const f32x16* acc, int kc) {
 // Keys stationary: workgroup (b, KV head, 128 keys), wave w owns keys
 // k0 + 32w .. +31 (one per lane of a half-wave pair).  Query tiles of 64 rows
 // of every query head of the group stream through LDS (Q, dO, log2-domain
-// LSE and Delta), double buffered.
+// LSE and Delta), double buffered; each tile is worked in two 32-row halves
+// (S and dP, then P and dS, then the dV and dK products), which keeps the
+// score registers of one half live at a time.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf16* __restrict__ dout,
-                                                      const float* __restrict__ delta, __bf16* __restrict__ dk,
-                                                      __bf16* __restrict__ dv) {
+                                                      const float* __restrict__ delta, const float* __restrict__ lse2,
+                                                      __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
   constexpr int BK = 128;        // keys per workgroup
   constexpr int BQ = 64;         // queries per tile
   constexpr int NDC = D / 16;    // contraction chunks over d
   constexpr int NDB = D / 32;    // 32-column blocks of d
-  constexpr int NQB = BQ / 32;   // 32-query blocks of a tile
-  constexpr int NQC = BQ / 16;   // 16-query chunks of a tile
-  constexpr int TILE = BQ * D * 2;
-  constexpr int STAGE = 2 * TILE + 2 * BQ * 4;  // Q, dO, lse, delta
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+  constexpr int NQB = BQ / 32;   // 32-query halves of a tile
+  using Tile = SwizzledTile<D, BQ>;
+  constexpr int TILE = Tile::BYTES;
+  constexpr int BPW = Tile::NBLK / 2;           // blocks per wave: waves 0-1 load Q, 2-3 dO
+  constexpr int STAGE = 2 * TILE + 2 * BQ * 4;  // Q, dO, lse2, delta
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const float sl2 = p.scale_log2;
@@ -191,36 +192,40 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf
   const int per_head = nqt > qt0 ? nqt - qt0 : 0;
   const int nsteps = per_head * p.group;
 
-  TileLoader<D, BQ> lq, ldo;
-  lq.init(tid);
-  ldo.init(tid);
+  // this wave's HBM -> LDS blocks: tensor (Q or dO) and its byte offsets
+  const bool loads_do = wu >= 2;
+  int voff[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) voff[i] = Tile::voff((wu & 1) * BPW + i, lane);
   float lse_reg = 0.0f, del_reg = 0.0f;
   auto step_src = [&](int s, int& h, int& q0) {
     h = kvh * p.group + s / per_head;
     q0 = (qt0 + s % per_head) * BQ;
   };
+  // issue the loads of step s into stage s & 1 (wave 0 also fetches the 64
+  // rows' lse2 and Delta into registers, stored by lstore)
   auto gload = [&](int s) {
     int h, q0;
     step_src(s, h, q0);
     const int64_t row0 = ((int64_t)b * p.H + h) * sq + q0;
-    lq.load((const __bf16*)p.q + row0 * D, sq - q0);
-    ldo.load(dout + row0 * D, sq - q0);
-    if (tid < BQ) {
-      const int i = q0 + tid;
-      // rows past the end and rows that saw no key take part with P = 0:
-      // their log-sum-exp becomes +inf
-      float l = i < sq ? p.lse[row0 + tid] : -INFINITY;
-      lse_reg = l == -INFINITY ? INFINITY : l * kLog2e;
-      del_reg = i < sq ? delta[row0 + tid] : 0.0f;
+    if (wu == 0) {
+      const int i = q0 + lane;
+      // rows past the end take part with P = 0
+      lse_reg = i < sq ? lse2[row0 + lane] : INFINITY;
+      del_reg = i < sq ? delta[row0 + lane] : 0.0f;
     }
+    const int nrows = sq - q0 < BQ ? sq - q0 : BQ;
+    const __bf16* src = loads_do ? dout + row0 * D : (const __bf16*)p.q + row0 * D;
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(src, nrows * 2 * D);
+    const unsigned dst = lds_u32(smem) + (s & 1) * STAGE + (loads_do ? TILE : 0) + (wu & 1) * BPW * 1024;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) load_lds16(rs, voff[i], 0, dst + i * 1024);
   };
   auto lstore = [&](int stage) {
-    unsigned char* base = smem + stage * STAGE;
-    lq.store(base);
-    ldo.store(base + TILE);
-    if (tid < BQ) {
-      ((float*)(base + 2 * TILE))[tid] = lse_reg;
-      ((float*)(base + 2 * TILE + BQ * 4))[tid] = del_reg;
+    if (wu == 0) {
+      float* base = (float*)(smem + stage * STAGE + 2 * TILE);
+      base[lane] = lse_reg;
+      base[BQ + lane] = del_reg;
     }
   };
 
@@ -229,11 +234,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf
   const int tr_row = 4 * (g16 >> 1) + (t16 >> 2);
   const int tr_col = 16 * (g16 & 1) + 4 * (t16 & 3);
 
-  if (nsteps > 0) {
-    gload(0);
-    lstore(0);
-  }
+  if (nsteps > 0) gload(0);
   __builtin_amdgcn_s_waitcnt(0);
+  lstore(0);
   __syncthreads();
 
   for (int s = 0; s < nsteps; ++s) {
@@ -246,45 +249,46 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf
     const unsigned char* tdo = tq + TILE;
     const float* tlse = (const float*)(tq + 2 * TILE);
     const float* tdel = tlse + BQ;
-    // this wave's keys see a query of the tile (causal) and exist
-    const bool live = kw0 < skv && (!CAUSAL || kw0 <= q0 + BQ - 1 + off);
-    if (live) {
-      f32x16 sacc[NQB], dpacc[NQB];
+    // Every wave runs every half, also where the causal mask hides all of
+    // it (the first tile of a key block, at most one per query head): the
+    // masked P and dS are 0, and an accumulator updated on every path stays
+    // in one register class (a branch around these MFMAs made the compiler
+    // copy all 128 accumulators between AGPRs and VGPRs every step).
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        sacc[qb] = f32x16{};
-        dpacc[qb] = f32x16{};
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qr0 = q0 + 32 * qb;
+      f32x16 sa = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int c = 0; c < NDC; ++c) {
-          sacc[qb] = mfma32(frag_rows<D>(tq, 32 * qb, c, l32, hh), kf[c], sacc[qb]);
-          dpacc[qb] = mfma32(frag_rows<D>(tdo, 32 * qb, c, l32, hh), vf[c], dpacc[qb]);
-        }
+      for (int c = 0; c < NDC; ++c) {
+        sa = mfma32(frag_rows<D>(tq, 32 * qb, c, l32, hh), kf[c], sa);
+        dp = mfma32(frag_rows<D>(tdo, 32 * qb, c, l32, hh), vf[c], dp);
       }
       // P and dS, one key per lane, query rows 32qb + 8(r/4) + 4hh + r%4
-      const bool partial = CAUSAL && (kw0 + 31 > q0 + off);
+      const bool partial = CAUSAL && (kw0 + 31 > qr0 + off);
+      if (partial) {
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
+        for (int r = 0; r < 16; ++r)
+          if (krow > qr0 + 8 * (r >> 2) + 4 * hh + (r & 3) + off) sa[r] = -INFINITY;
+      }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int rr = 32 * qb + 8 * g + 4 * hh;
-          const f32x4 lv = *(const f32x4*)(tlse + rr);
-          const f32x4 dl = *(const f32x4*)(tdel + rr);
+      for (int g = 0; g < 4; ++g) {
+        const int rr = 32 * qb + 8 * g + 4 * hh;
+        const f32x4 lv = *(const f32x4*)(tlse + rr);
+        const f32x4 dl = *(const f32x4*)(tdel + rr);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float sv = sacc[qb][r];
-            if (partial && krow > q0 + rr + e + off) sv = -INFINITY;
-            const float pv = fast_exp2(fmaf(sv, sl2, -lv[e]));
-            sacc[qb][r] = pv;
-            dpacc[qb][r] = pv * (dpacc[qb][r] - dl[e]);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const float pv = fast_exp2(fmaf(sa[r], sl2, -lv[e]));
+          sa[r] = pv;
+          dp[r] = pv * (dp[r] - dl[e]);
         }
       }
-      // dV^T += dO^T P, dK^T += Q^T dS (16 queries per step)
+      // dV^T += dO^T P, dK^T += Q^T dS (16 queries per product)
 #pragma unroll
-      for (int qc = 0; qc < NQC; ++qc) {
-        const bf16x8 pb = chunk_bf16(sacc, qc);
-        const bf16x8 sb = chunk_bf16(dpacc, qc);
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int qc = 2 * qb + h2;
+        const bf16x8 pb = half_bf16(sa, h2);
+        const bf16x8 sb = half_bf16(dp, h2);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           dvt[db] = mfma32(frag_cols<D>(tdo, qc, db, tr_row, tr_col), pb, dvt[db]);
@@ -292,6 +296,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf
         }
       }
     }
+    // the next stage's loads have landed (its lse2 / Delta are then stored)
+    // before the barrier that publishes it
+    __builtin_amdgcn_s_waitcnt(0);
     if (s + 1 < nsteps) lstore(stage ^ 1);
     __syncthreads();
   }
@@ -321,22 +328,26 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf
 
 // Queries stationary: workgroup (b, query head, 128 queries), wave w owns
 // queries q0 + 32w .. +31 (one per lane of a half-wave pair); key tiles of 64
-// rows stream through LDS, double buffered.
+// rows stream through LDS, double buffered, each worked in two 32-key
+// halves.  Two workgroups share a CU.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void dq_kernel(const Params p, const __bf16* __restrict__ dout,
-                                                    const float* __restrict__ delta, __bf16* __restrict__ dq) {
+__global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16* __restrict__ dout,
+                                                    const float* __restrict__ delta, const float* __restrict__ lse2,
+                                                    __bf16* __restrict__ dq) {
   constexpr int BMQ = 128;
   constexpr int BN = 64;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int NKB = BN / 32;
-  constexpr int NKC = BN / 16;
-  constexpr int TILE = BN * D * 2;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * TILE];
+  using Tile = SwizzledTile<D, BN>;
+  constexpr int TILE = Tile::BYTES;
+  constexpr int BPW = Tile::NBLK / 2;  // blocks per wave: waves 0-1 load K, 2-3 V
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const float sl2 = p.scale_log2;
@@ -363,15 +374,14 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(const Params p, const __bf16
   const __bf16* __restrict__ V = (const __bf16*)p.v + kv0 * D;
 
   bf16x8 qf[NDC], dof[NDC];
-  float neg_lse = -INFINITY, del = 0.0f;  // -LSE log2(e) of this lane's row
+  float neg_lse = -INFINITY, del = 0.0f;  // -LSE log2(e) of this lane's row (-inf: P = 0)
   if (qrow < sq) {
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
       qf[c] = *(const bf16x8*)(Q + (int64_t)qrow * D + 16 * c + 8 * hh);
       dof[c] = *(const bf16x8*)(dO + (int64_t)qrow * D + 16 * c + 8 * hh);
     }
-    const float l = p.lse[row0 + qrow];
-    neg_lse = l == -INFINITY ? -INFINITY : -l * kLog2e;  // no key seen: P = 0
+    neg_lse = -lse2[row0 + qrow];
     del = delta[row0 + qrow];
   } else {
 #pragma unroll
@@ -390,17 +400,17 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(const Params p, const __bf16
     w_end = CAUSAL ? causal_kv_end(w_hi, off, skv) : skv;
   }
 
-  TileLoader<D, BN> lk, lv;
-  lk.init(tid);
-  lv.init(tid);
+  const bool loads_v = wu >= 2;
+  int voff[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) voff[i] = Tile::voff((wu & 1) * BPW + i, lane);
   auto gload = [&](int t) {
-    const int k0 = t * BN;
-    lk.load(K + (int64_t)k0 * D, skv - k0);
-    lv.load(V + (int64_t)k0 * D, skv - k0);
-  };
-  auto lstore = [&](int stage) {
-    lk.store(smem + stage * 2 * TILE);
-    lv.store(smem + stage * 2 * TILE + TILE);
+    const int kb0 = t * BN;
+    const int nrows = skv - kb0 < BN ? skv - kb0 : BN;
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc((loads_v ? V : K) + (int64_t)kb0 * D, nrows * 2 * D);
+    const unsigned dst = lds_u32(smem) + (t & 1) * 2 * TILE + (loads_v ? TILE : 0) + (wu & 1) * BPW * 1024;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) load_lds16(rs, voff[i], 0, dst + i * 1024);
   };
 
   const int g16 = lane >> 4;
@@ -412,10 +422,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(const Params p, const __bf16
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqt[db] = f32x16{};
 
-  if (nt > 0) {
-    gload(0);
-    lstore(0);
-  }
+  if (nt > 0) gload(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -424,44 +431,44 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(const Params p, const __bf16
     const int c_lim = qrow + off + 1;
     lim = c_lim < lim ? c_lim : lim;
   }
+  // keys < lim are visible; compared as lim - 4hh against a wave-uniform key
+  const int lim_h = lim - 4 * hh;
 
   for (int t = 0; t < nt; ++t) {
     const int stage = t & 1;
     const int k0 = t * BN;
     if (t + 1 < nt) gload(t + 1);
-    if (k0 < w_end) {
-      const unsigned char* tk = smem + stage * 2 * TILE;
-      const unsigned char* tv = tk + TILE;
-      f32x16 st[NKB], dpt[NKB];  // S^T, dP^T: key rows, this lane's query
+    const unsigned char* tk = smem + stage * 2 * TILE;
+    const unsigned char* tv = tk + TILE;
 #pragma unroll
-      for (int kbi = 0; kbi < NKB; ++kbi) {
-        st[kbi] = f32x16{};
-        dpt[kbi] = f32x16{};
+    for (int kbi = 0; kbi < NKB; ++kbi) {
+      const int kb = k0 + 32 * kbi;
+      // no row of this wave sees a key of this half
+      if (kb >= w_end) continue;
+      f32x16 st = f32x16{}, dpt = f32x16{};  // S^T, dP^T: key rows, this lane's query
 #pragma unroll
-        for (int c = 0; c < NDC; ++c) {
-          st[kbi] = mfma32(frag_rows<D>(tk, 32 * kbi, c, l32, hh), qf[c], st[kbi]);
-          dpt[kbi] = mfma32(frag_rows<D>(tv, 32 * kbi, c, l32, hh), dof[c], dpt[kbi]);
-        }
+      for (int c = 0; c < NDC; ++c) {
+        st = mfma32(frag_rows<D>(tk, 32 * kbi, c, l32, hh), qf[c], st);
+        dpt = mfma32(frag_rows<D>(tv, 32 * kbi, c, l32, hh), dof[c], dpt);
       }
-      const bool partial = (k0 + BN > skv) || (CAUSAL && (k0 + BN - 1 > qw0 + off));
+      const bool partial = (kb + 32 > skv) || (CAUSAL && (kb + 31 > qw0 + off));
 #pragma unroll
-      for (int kbi = 0; kbi < NKB; ++kbi)
+      for (int r = 0; r < 16; ++r) {  // key kb + 8(r/4) + 4hh + r%4
+        float sv = st[r];
+        if (partial && kb + 8 * (r >> 2) + (r & 3) >= lim_h) sv = -INFINITY;
+        const float pv = fast_exp2(fmaf(sv, sl2, neg_lse));
+        dpt[r] = pv * (dpt[r] - del);
+      }
+      // dQ^T += K^T dS^T over 16-key chunks
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float sv = st[kbi][r];
-          if (partial && k0 + 32 * kbi + 8 * (r >> 2) + 4 * hh + (r & 3) >= lim) sv = -INFINITY;
-          const float pv = fast_exp2(fmaf(sv, sl2, neg_lse));
-          dpt[kbi][r] = pv * (dpt[kbi][r] - del);
-        }
-      // dQ^T += K^T dS^T over 16-key steps
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 sb = half_bf16(dpt, h2);
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const bf16x8 sb = chunk_bf16(dpt, kc);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) dqt[db] = mfma32(frag_cols<D>(tk, kc, db, tr_row, tr_col), sb, dqt[db]);
+        for (int db = 0; db < NDB; ++db)
+          dqt[db] = mfma32(frag_cols<D>(tk, 2 * kbi + h2, db, tr_row, tr_col), sb, dqt[db]);
       }
     }
-    if (t + 1 < nt) lstore(stage ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -481,40 +488,41 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(const Params p, const __bf16
 }
 
 template <int D>
-hipError_t launch_bwd_d(const Params& p, const __bf16* dout, float* delta, __bf16* dq, __bf16* dk, __bf16* dv,
-                        hipStream_t st) {
+hipError_t launch_bwd_d(const Params& p, const __bf16* dout, float* delta, float* lse2, __bf16* dq, __bf16* dk,
+                        __bf16* dv, hipStream_t st) {
   const long rows = (long)p.B * p.H * p.Sq;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
-                     (const __bf16*)p.o, dout, delta, rows);
+                     (const __bf16*)p.o, dout, p.lse, delta, lse2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.Skv > 0) {
     const long g1 = (long)p.B * p.Hkv * ceil_div(p.Skv, 128);
     if (p.causal)
-      hipLaunchKernelGGL((dkdv_kernel<D, true>), dim3((unsigned)g1), dim3(256), 0, st, p, dout, delta, dk, dv);
+      hipLaunchKernelGGL((dkdv_kernel<D, true>), dim3((unsigned)g1), dim3(256), 0, st, p, dout, delta, lse2, dk, dv);
     else
-      hipLaunchKernelGGL((dkdv_kernel<D, false>), dim3((unsigned)g1), dim3(256), 0, st, p, dout, delta, dk, dv);
+      hipLaunchKernelGGL((dkdv_kernel<D, false>), dim3((unsigned)g1), dim3(256), 0, st, p, dout, delta, lse2, dk,
+                         dv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const long g2 = (long)p.B * p.H * ceil_div(p.Sq, 128);
   if (p.causal)
-    hipLaunchKernelGGL((dq_kernel<D, true>), dim3((unsigned)g2), dim3(256), 0, st, p, dout, delta, dq);
+    hipLaunchKernelGGL((dq_kernel<D, true>), dim3((unsigned)g2), dim3(256), 0, st, p, dout, delta, lse2, dq);
   else
-    hipLaunchKernelGGL((dq_kernel<D, false>), dim3((unsigned)g2), dim3(256), 0, st, p, dout, delta, dq);
+    hipLaunchKernelGGL((dq_kernel<D, false>), dim3((unsigned)g2), dim3(256), 0, st, p, dout, delta, lse2, dq);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_backward(const Params& p, const void* dout, float* delta, void* dq, void* dk, void* dv,
-                           hipStream_t st) {
+hipError_t launch_backward(const Params& p, const void* dout, float* delta, float* lse2, void* dq, void* dk,
+                           void* dv, hipStream_t st) {
   if ((long)p.B * p.H * p.Sq <= 0) return hipSuccess;
   if (p.d == 128)
-    return launch_bwd_d<128>(p, (const __bf16*)dout, delta, (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, st);
+    return launch_bwd_d<128>(p, (const __bf16*)dout, delta, lse2, (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, st);
   if (p.d == 64)
-    return launch_bwd_d<64>(p, (const __bf16*)dout, delta, (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, st);
+    return launch_bwd_d<64>(p, (const __bf16*)dout, delta, lse2, (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, st);
   return hipErrorInvalidValue;
 }
 

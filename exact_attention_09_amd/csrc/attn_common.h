@@ -137,6 +137,43 @@ __device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int so
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+#pragma clang diagnostic push
+// m0 is written by these loads only; no other instruction in the kernel reads it
+#pragma clang diagnostic ignored "-Winline-asm"
+// HBM -> LDS without registers: 16 bytes per lane at LDS address m0 + 16 *
+// lane (out-of-range bytes arrive as zeros).  Issued as inline assembly so
+// that the compiler, which cannot tell which LDS bytes they write, does not
+// wait for them before every LDS read; a kernel waits for them itself
+// (vmcnt) before the barrier that publishes the buffer they fill.  lds_addr
+// must be wave-uniform.
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, int voff, int soff, unsigned lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(soff), "s"(lds_addr)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ inline int64_t uniform64(int64_t x) {
+  const uint64_t u = (uint64_t)x;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// buffer descriptor of a wave-uniform base and size, kept in scalar registers
+// (the loads above take it as a scalar operand)
+__device__ inline __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const int64_t b = uniform64((int64_t)(uintptr_t)base);
+  return make_rsrc((const void*)(uintptr_t)b, __builtin_amdgcn_readfirstlane(bytes));
+}
+
+__device__ inline unsigned lds_u32(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // ---------------------------------------------------------------- LDS swizzle
 //
 // A K or V tile sits in LDS row-major (one key per row, d contiguous) with

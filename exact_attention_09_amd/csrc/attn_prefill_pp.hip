@@ -76,43 +76,6 @@ constexpr int kMaxListedSeqs = 1024;
 #define ATTN_PP_AHEAD 3
 #endif
 
-#pragma clang diagnostic push
-// m0 is written by these loads only; no other instruction in the kernel reads it
-#pragma clang diagnostic ignored "-Winline-asm"
-// HBM -> LDS without registers: 16 bytes per lane at LDS address m0 + 16 *
-// lane (out-of-range bytes arrive as zeros).  Issued as inline assembly so
-// that the compiler, which cannot tell the ring stages apart, does not wait
-// for these loads before every LDS read; the kernel waits for them itself
-// (vmcnt) before the barrier that publishes a stage.  lds_addr must be
-// wave-uniform.
-__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, int voff, int soff, unsigned lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %3\n\t"
-      "buffer_load_dwordx4 %0, %1, %2 offen lds"
-      :
-      : "v"(voff), "s"(r), "s"(soff), "s"(lds_addr)
-      : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ inline int64_t uniform64(int64_t x) {
-  const uint64_t u = (uint64_t)x;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
-// buffer descriptor of a wave-uniform base and size, kept in scalar registers
-// (the loads above take it as a scalar operand)
-__device__ inline __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
-  const int64_t b = uniform64((int64_t)(uintptr_t)base);
-  return make_rsrc((const void*)(uintptr_t)b, __builtin_amdgcn_readfirstlane(bytes));
-}
-
-__device__ inline unsigned lds_u32(const void* p) {
-  return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
-}
-
 // LOCAL: the sliding-window / sink variant (causal only); off, the kernel is
 // compiled without any of its code.  BSHD: [B, S, H, d] tensors (row
 // strides H d and Hkv d, known at run time); off, rows are d apart and every

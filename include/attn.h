@@ -201,8 +201,9 @@ attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cac
  * o and lse must be the forward outputs for the same q, k, v, scale and
  * causal flag.  P and dS are rounded to bf16 (nearest even) for the products
  * that use them; all sums are fp32.  The workspace (opts, may be NULL) holds
- * Delta: attn_bwd_workspace_bytes(B, H, Sq) bytes, 256-byte aligned, else it
- * is allocated stream-ordered.  Validation, errors and ordering on `stream`
+ * Delta and the LSE in log2 units, one fp32 per query row each:
+ * attn_bwd_workspace_bytes(B, H, Sq) bytes, 256-byte aligned, else it is
+ * allocated stream-ordered.  Validation, errors and ordering on `stream`
  * as for attn_fwd_ex; opts->num_splits is ignored. */
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                      void* dq, void* dk, void* dv, int B, int H, int Hkv, int Sq, int Skv, int d, float scale,

@@ -222,5 +222,6 @@ def test_bwd_rejects_before_any_hip_call(lib, kw, status):
 def test_bwd_empty_and_workspace(lib):
     assert bwd_call(lib, B=0) == ea.ATTN_OK
     assert bwd_call(lib, Sq=0, Skv=0) == ea.ATTN_OK
-    assert ea.attn_bwd_workspace_bytes(2, 4, 100) == 3328  # 3200 bytes of Delta, rounded to 256
+    # Delta and the log2 LSE: 3200 bytes each, each rounded up to 256
+    assert ea.attn_bwd_workspace_bytes(2, 4, 100) == 2 * 3328
     assert ea.attn_bwd_workspace_bytes(-1, 4, 100) == 0
