@@ -28,6 +28,8 @@
 // 16-byte chunk swizzle of attn_common.h; the transposed operands are read
 // with ds_read_b64_tr_b16.  P and dS are rounded to bf16 (nearest even) for
 // the products that consume them; every accumulation is fp32.
+#include <utility>
+
 #include "attn_common.h"
 #include "attn_internal.h"
 
@@ -36,6 +38,25 @@ namespace attn {
 namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
+
+#ifndef ATTN_BWD_AHEAD
+#define ATTN_BWD_AHEAD 3
+#endif
+#ifndef ATTN_BWD_AHEAD_DQ
+#define ATTN_BWD_AHEAD_DQ 1
+#endif
+
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N-1>), expanded at
+// compile time (every index a constant, so arrays indexed by it stay in
+// registers however long the sequence)
+template <typename F, int... I>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // ---------------------------------------------------------------- Delta
 
@@ -254,47 +275,77 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf
     // masked P and dS are 0, and an accumulator updated on every path stays
     // in one register class (a branch around these MFMAs made the compiler
     // copy all 128 accumulators between AGPRs and VGPRs every step).
+    //
+    // The step is four MFMA phases of NQK = d/8 MFMAs each:
+    //   A: S and dP of rows 0-31      B: S and dP of rows 32-63
+    //   C: dV and dK of rows 0-31     D: dV and dK of rows 32-63
+    // written out as a software pipeline: MFMA i takes its A operand from a
+    // register ring filled AH MFMAs earlier, and the vector work of rows
+    // 0-31 (mask, P, dS, bf16) is cut into one element per MFMA of B, that
+    // of rows 32-63 into one per MFMA of C, so it runs while the matrix
+    // cores are busy.  sched_barrier fences keep the compiler from
+    // regrouping the slots (left to itself it read each operand one MFMA
+    // ahead and ran the vector work between MFMA blocks: 22 % slower).
+    f32x16 sa[NQB], dp[NQB];
+    bf16x8 pb[NQB][2], sb[NQB][2];
+    {
+      constexpr int NQK = 2 * NDC;
+      constexpr int NM = 4 * NQK;
+      constexpr int AH = ATTN_BWD_AHEAD;
+      constexpr int R = AH + 1;
+      auto fetch = [&](const int i) -> bf16x8 {
+        const int ph = i / NQK, j = i % NQK;
+        if (ph < 2) return frag_rows<D>((j & 1) ? tdo : tq, 32 * ph, j >> 1, l32, hh);
+        const int qc = 2 * (ph - 2) + j / (2 * NDB), db = (j % (2 * NDB)) >> 1;
+        return frag_cols<D>((j & 1) ? tq : tdo, qc, db, tr_row, tr_col);
+      };
+      constexpr int EPS = (16 + NQK - 1) / NQK;  // vector elements per MFMA slot
+      bf16x8 ring[R];
+      f32x4 lv[NQB][4], dl[NQB][4];
+      auto read_stats = [&](const int qb) {
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int qr0 = q0 + 32 * qb;
-      f32x16 sa = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NDC; ++c) {
-        sa = mfma32(frag_rows<D>(tq, 32 * qb, c, l32, hh), kf[c], sa);
-        dp = mfma32(frag_rows<D>(tdo, 32 * qb, c, l32, hh), vf[c], dp);
-      }
-      // P and dS, one key per lane, query rows 32qb + 8(r/4) + 4hh + r%4
-      const bool partial = CAUSAL && (kw0 + 31 > qr0 + off);
-      if (partial) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (krow > qr0 + 8 * (r >> 2) + 4 * hh + (r & 3) + off) sa[r] = -INFINITY;
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int rr = 32 * qb + 8 * g + 4 * hh;
-        const f32x4 lv = *(const f32x4*)(tlse + rr);
-        const f32x4 dl = *(const f32x4*)(tdel + rr);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          const float pv = fast_exp2(fmaf(sa[r], sl2, -lv[e]));
-          sa[r] = pv;
-          dp[r] = pv * (dp[r] - dl[e]);
+        for (int g = 0; g < 4; ++g) {
+          lv[qb][g] = *(const f32x4*)(tlse + 32 * qb + 8 * g + 4 * hh);
+          dl[qb][g] = *(const f32x4*)(tdel + 32 * qb + 8 * g + 4 * hh);
         }
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS (16 queries per product)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int qc = 2 * qb + h2;
-        const bf16x8 pb = half_bf16(sa, h2);
-        const bf16x8 sb = half_bf16(dp, h2);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dvt[db] = mfma32(frag_cols<D>(tdo, qc, db, tr_row, tr_col), pb, dvt[db]);
-          dkt[db] = mfma32(frag_cols<D>(tq, qc, db, tr_row, tr_col), sb, dkt[db]);
+      };
+      auto vec_elem = [&](const int qb, const int r) {
+        const int g = r >> 2, e = r & 3;
+        float sv = sa[qb][r];
+        if (CAUSAL) sv = krow > q0 + 32 * qb + 8 * g + 4 * hh + e + off ? -INFINITY : sv;
+        const float pv = fast_exp2(fmaf(sv, sl2, -lv[qb][g][e]));
+        sa[qb][r] = pv;
+        dp[qb][r] = pv * (dp[qb][r] - dl[qb][g][e]);
+        if (r == 7 || r == 15) {
+          pb[qb][r >> 3] = half_bf16(sa[qb], r >> 3);
+          sb[qb][r >> 3] = half_bf16(dp[qb], r >> 3);
         }
-      }
+      };
+      static_for<AH>([&](auto ic) { ring[decltype(ic)::value] = fetch(decltype(ic)::value); });
+      sa[0] = sa[1] = dp[0] = dp[1] = f32x16{};
+      static_for<NM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int ph = i / NQK, j = i % NQK;
+        if (i + AH < NM) ring[(i + AH) % R] = fetch(i + AH);
+        // a half's row statistics, two MFMAs before its vector work starts
+        if (ph < 2 && j == NQK - 2) read_stats(ph);
+        const bf16x8 a = ring[i % R];
+        if (ph < 2) {
+          if (j & 1) dp[ph] = mfma32(a, vf[j >> 1], dp[ph]);
+          else sa[ph] = mfma32(a, kf[j >> 1], sa[ph]);
+        } else {
+          const int qb = ph - 2, h2 = j / (2 * NDB), db = (j % (2 * NDB)) >> 1;
+          if (j & 1) dkt[db] = mfma32(a, sb[qb][h2], dkt[db]);
+          else dvt[db] = mfma32(a, pb[qb][h2], dvt[db]);
+        }
+        // EPS elements (of 16) of the previous half's vector work per MFMA
+        if (ph == 1 || ph == 2) {
+#pragma unroll
+          for (int x = 0; x < EPS; ++x)
+            if (j * EPS + x < 16) vec_elem(ph - 1, j * EPS + x);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
     // the next stage's loads have landed (its lse2 / Delta are then stored)
     // before the barrier that publishes it
@@ -440,33 +491,69 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
     if (t + 1 < nt) gload(t + 1);
     const unsigned char* tk = smem + stage * 2 * TILE;
     const unsigned char* tv = tk + TILE;
-#pragma unroll
-    for (int kbi = 0; kbi < NKB; ++kbi) {
-      const int kb = k0 + 32 * kbi;
-      // no row of this wave sees a key of this half
-      if (kb >= w_end) continue;
-      f32x16 st = f32x16{}, dpt = f32x16{};  // S^T, dP^T: key rows, this lane's query
-#pragma unroll
-      for (int c = 0; c < NDC; ++c) {
-        st = mfma32(frag_rows<D>(tk, 32 * kbi, c, l32, hh), qf[c], st);
-        dpt = mfma32(frag_rows<D>(tv, 32 * kbi, c, l32, hh), dof[c], dpt);
-      }
-      const bool partial = (kb + 32 > skv) || (CAUSAL && (kb + 31 > qw0 + off));
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {  // key kb + 8(r/4) + 4hh + r%4
-        float sv = st[r];
-        if (partial && kb + 8 * (r >> 2) + (r & 3) >= lim_h) sv = -INFINITY;
+    // skip the tiles no row of this wave sees (causal); a branch around the
+    // whole step, so the accumulators stay where they are
+    if (k0 < w_end) {
+      // Four MFMA phases, the same software pipeline as the dK/dV kernel:
+      //   A: S^T and dP^T of keys 0-31    B: S^T and dP^T of keys 32-63
+      //   C: dQ^T from keys 0-31          D: dQ^T from keys 32-63
+      // with the vector work (mask, P, dS, bf16) of keys 0-31 spread over
+      // the MFMAs of B and that of keys 32-63 over those of C, and every A
+      // operand read AH MFMAs ahead into a register ring (one ahead: at two
+      // waves per SIMD the other wave hides the rest of the latency, and a
+      // deeper ring no longer fits the 256 registers).
+      constexpr int NSD = 2 * NDC;  // S^T and dP^T MFMAs of a half
+      constexpr int NG = 2 * NDB;   // dQ^T MFMAs of a half
+      constexpr int NM = 2 * NSD + 2 * NG;
+      constexpr int AH = ATTN_BWD_AHEAD_DQ;
+      constexpr int R = AH + 1;
+      constexpr int EPS_B = (16 + NSD - 1) / NSD;  // vector elements per MFMA slot of B
+      constexpr int EPS_C = (16 + NG - 1) / NG;    // ... of C
+      f32x16 st[NKB], dpt[NKB];  // S^T, dP^T: key rows, this lane's query
+      bf16x8 sb[NKB][2];
+      bf16x8 ring[R];
+      auto fetch = [&](const int i) -> bf16x8 {
+        if (i < 2 * NSD) {
+          const int kbi = i / NSD, j = i % NSD;
+          return frag_rows<D>((j & 1) ? tv : tk, 32 * kbi, j >> 1, l32, hh);
+        }
+        const int i2 = i - 2 * NSD, kbi = i2 / NG, j = i2 % NG;
+        return frag_cols<D>(tk, 2 * kbi + j / NDB, j % NDB, tr_row, tr_col);
+      };
+      // key k0 + 32kbi + 8(r/4) + 4hh + r%4 of this lane's query
+      auto vec_elem = [&](const int kbi, const int r) {
+        float sv = st[kbi][r];
+        if (CAUSAL) sv = k0 + 32 * kbi + 8 * (r >> 2) + (r & 3) >= lim_h ? -INFINITY : sv;
         const float pv = fast_exp2(fmaf(sv, sl2, neg_lse));
-        dpt[r] = pv * (dpt[r] - del);
-      }
-      // dQ^T += K^T dS^T over 16-key chunks
+        dpt[kbi][r] = pv * (dpt[kbi][r] - del);
+        if (r == 7 || r == 15) sb[kbi][r >> 3] = half_bf16(dpt[kbi], r >> 3);
+      };
+      static_for<AH>([&](auto ic) { ring[decltype(ic)::value] = fetch(decltype(ic)::value); });
+      st[0] = st[1] = dpt[0] = dpt[1] = f32x16{};
+      static_for<NM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if (i + AH < NM) ring[(i + AH) % R] = fetch(i + AH);
+        const bf16x8 a = ring[i % R];
+        if (i < 2 * NSD) {
+          constexpr int kbi = i / NSD, j = i % NSD;
+          if (j & 1) dpt[kbi] = mfma32(a, dof[j >> 1], dpt[kbi]);
+          else st[kbi] = mfma32(a, qf[j >> 1], st[kbi]);
+          if (kbi == 1) {
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 sb = half_bf16(dpt, h2);
+            for (int x = 0; x < EPS_B; ++x)
+              if (j * EPS_B + x < 16) vec_elem(0, j * EPS_B + x);
+          }
+        } else {
+          constexpr int i2 = i - 2 * NSD, kbi = i2 / NG, j = i2 % NG;
+          dqt[j % NDB] = mfma32(a, sb[kbi][j / NDB], dqt[j % NDB]);
+          if (kbi == 0) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          dqt[db] = mfma32(frag_cols<D>(tk, 2 * kbi + h2, db, tr_row, tr_col), sb, dqt[db]);
-      }
+            for (int x = 0; x < EPS_C; ++x)
+              if (j * EPS_C + x < 16) vec_elem(1, j * EPS_C + x);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
