@@ -166,9 +166,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf
 
   // causal: key tiles in order of decreasing work (a key tile's query range
   // shrinks as the keys move right), so the light tiles fill the tail
+  // non-causal: XCD-aware, each XCD walks a contiguous range of items, so
+  // the key tiles of one KV head run together and share its Q/dO stream in
+  // that XCD's L2 (the grid is padded to a multiple of 8; padding exits)
   const int ktiles = ceil_div(p.Skv, BK);
-  const int item = blockIdx.x;
   const int nbk = p.B * p.Hkv;
+  const int item = CAUSAL ? (int)blockIdx.x : xcd_remap((int)blockIdx.x, nbk * ktiles);
+  if (item < 0) return;
   const int kt = CAUSAL ? item / nbk : item % ktiles;
   const int bk = CAUSAL ? item - kt * nbk : item / ktiles;  // b * Hkv + kvh
   const int b = bk / p.Hkv;
@@ -405,9 +409,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
 
   // causal: query tiles in order of decreasing work (the last tiles see the
   // most keys)
+  // non-causal: XCD-aware as in the dK/dV kernel (the query tiles of a head
+  // share its K/V stream in one L2)
   const int qtiles = ceil_div(p.Sq, BMQ);
-  const int item = blockIdx.x;
   const int nbh = p.B * p.H;
+  const int item = CAUSAL ? (int)blockIdx.x : xcd_remap((int)blockIdx.x, nbh * qtiles);
+  if (item < 0) return;
   const int bh = CAUSAL ? item % nbh : item / qtiles;
   const int tile = CAUSAL ? qtiles - 1 - item / nbh : item - bh * qtiles;
   const int b = bh / p.H;
@@ -583,8 +590,10 @@ hipError_t launch_bwd_d(const Params& p, const __bf16* dout, float* delta, float
                      (const __bf16*)p.o, dout, p.lse, delta, lse2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // non-causal grids are padded to a multiple of 8 for the XCD mapping
+  auto pad8 = [](long n) { return (n + 7) / 8 * 8; };
   if (p.Skv > 0) {
-    const long g1 = (long)p.B * p.Hkv * ceil_div(p.Skv, 128);
+    const long g1 = p.causal ? (long)p.B * p.Hkv * ceil_div(p.Skv, 128) : pad8((long)p.B * p.Hkv * ceil_div(p.Skv, 128));
     if (p.causal)
       hipLaunchKernelGGL((dkdv_kernel<D, true>), dim3((unsigned)g1), dim3(256), 0, st, p, dout, delta, lse2, dk, dv);
     else
@@ -593,7 +602,7 @@ hipError_t launch_bwd_d(const Params& p, const __bf16* dout, float* delta, float
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const long g2 = (long)p.B * p.H * ceil_div(p.Sq, 128);
+  const long g2 = p.causal ? (long)p.B * p.H * ceil_div(p.Sq, 128) : pad8((long)p.B * p.H * ceil_div(p.Sq, 128));
   if (p.causal)
     hipLaunchKernelGGL((dq_kernel<D, true>), dim3((unsigned)g2), dim3(256), 0, st, p, dout, delta, lse2, dq);
   else
