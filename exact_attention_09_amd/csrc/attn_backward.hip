@@ -28,8 +28,6 @@
 // 16-byte chunk swizzle of attn_common.h; the transposed operands are read
 // with ds_read_b64_tr_b16.  P and dS are rounded to bf16 (nearest even) for
 // the products that consume them; every accumulation is fp32.
-#include <utility>
-
 #include "attn_common.h"
 #include "attn_internal.h"
 
@@ -45,18 +43,6 @@ constexpr float kLog2e = 1.44269504088896340736f;
 #ifndef ATTN_BWD_AHEAD_DQ
 #define ATTN_BWD_AHEAD_DQ 1
 #endif
-
-// f(integral_constant<int, 0>) .. f(integral_constant<int, N-1>), expanded at
-// compile time (every index a constant, so arrays indexed by it stay in
-// registers however long the sequence)
-template <typename F, int... I>
-__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ inline void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 // ---------------------------------------------------------------- Delta
 

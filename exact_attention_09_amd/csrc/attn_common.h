@@ -5,6 +5,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <utility>
 #include <stdint.h>
 
 namespace attn {
@@ -172,6 +174,18 @@ __device__ inline __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int byte
 
 __device__ inline unsigned lds_u32(const void* p) {
   return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N-1>), expanded at
+// compile time (every index a constant, so arrays indexed by it stay in
+// registers however long the sequence)
+template <typename F, int... I>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // ---------------------------------------------------------------- LDS swizzle

@@ -279,26 +279,56 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
         if (do_pv && do_qk) {
           // steady state: the 16 P~V and 16 QK^T MFMAs are independent, so
           // they are issued alternately, each with its operand read a few
-          // MFMAs ahead (order pinned with sched_group_barrier: 0x100 LDS
-          // read, 0x008 MFMA)
+          // MFMAs ahead
+          if constexpr (LOCAL) {
+            // The same order written out MFMA pair by MFMA pair, each operand
+            // read AHEAD pairs earlier into a register ring, and fenced with
+            // sched_barrier.  In this instantiation the scheduler drops the
+            // sched_group_barrier pins below (every read then waited for
+            // lgkmcnt(0) before its MFMA: 23-29 % slower); where the pins hold,
+            // they are 0.5-1.5 % faster than this form.
+            constexpr int AH = ATTN_PP_AHEAD;
+            constexpr int R = AH + 1;
+            bf16x8 vr[R], kr[R];
 #pragma unroll
-          for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = f32x16{};
+            for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = f32x16{};
+            static_for<AH>([&](auto ic) {
+              constexpr int i = decltype(ic)::value;
+              vr[i] = vfrag(i / NDB, i % NDB);
+              kr[i] = kfrag(i / NKB, i % NKB);
+            });
+            static_for<NPV>([&](auto ic) {
+              constexpr int i = decltype(ic)::value;
+              constexpr int kc = i / NDB, db = i % NDB;
+              oacc[db] = mfma32(vr[i % R], pb[kc], oacc[db]);
+              if constexpr (i + AH < NPV) vr[(i + AH) % R] = vfrag((i + AH) / NDB, (i + AH) % NDB);
+              constexpr int c = i / NKB, kbi = i % NKB;
+              s[kbi] = mfma32(kr[i % R], qf[c], s[kbi]);
+              if constexpr (i + AH < NPV) kr[(i + AH) % R] = kfrag((i + AH) / NKB, (i + AH) % NKB);
+              __builtin_amdgcn_sched_barrier(0);
+            });
+          } else {
+            // (order pinned with sched_group_barrier: 0x100 LDS read, 0x008
+            // MFMA)
 #pragma unroll
-          for (int i = 0; i < NPV; ++i) {
-            const int kc = i / NDB, db = i % NDB;
-            oacc[db] = mfma32(vfrag(kc, db), pb[kc], oacc[db]);
-            const int c = i / NKB, kbi = i % NKB;
-            s[kbi] = mfma32(kfrag(c, kbi), qf[c], s[kbi]);
+            for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = f32x16{};
+#pragma unroll
+            for (int i = 0; i < NPV; ++i) {
+              const int kc = i / NDB, db = i % NDB;
+              oacc[db] = mfma32(vfrag(kc, db), pb[kc], oacc[db]);
+              const int c = i / NKB, kbi = i % NKB;
+              s[kbi] = mfma32(kfrag(c, kbi), qf[c], s[kbi]);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 3 * ATTN_PP_AHEAD, 0);
+#pragma unroll
+            for (int i = 0; i < NPV - ATTN_PP_AHEAD; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * ATTN_PP_AHEAD, 0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x100, 3 * ATTN_PP_AHEAD, 0);
-#pragma unroll
-          for (int i = 0; i < NPV - ATTN_PP_AHEAD; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 2 * ATTN_PP_AHEAD, 0);
         } else {
         bf16x8 kf[2][NKB];
         if (do_pv) {
