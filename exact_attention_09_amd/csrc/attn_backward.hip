@@ -11,10 +11,10 @@
 //
 // Three kernels, no atomics, fixed summation orders (bitwise reproducible):
 //   * delta_kernel: Delta in fp32;
-//   * dkdv_kernel: one workgroup per (batch, KV head, 128 keys); each wave
-//     keeps its 32 keys' K and V rows in registers and walks the query tiles
-//     of every query head of the group, so the grouped-query sum happens in
-//     registers;
+//   * dkdv_pair_kernel: one workgroup per (batch, KV head, 128 keys); a pair
+//     of waves keeps 32 keys' K and V rows in registers (one each) and walks
+//     the query tiles of every query head of the group, so the grouped-query
+//     sum happens in registers;
 //   * dq_kernel: one workgroup per (batch, query head, 128 queries); each
 //     wave keeps its 32 queries' Q and dO rows in registers and walks the key
 //     tiles.  dQ costs a second computation of S and dP instead of atomic
@@ -22,7 +22,7 @@
 //
 // Both tile kernels use v_mfma_f32_32x32x16_bf16 with the accumulator
 // arranged so that the exponentiated scores are directly the B operand of the
-// next product (as in the forward kernels): dkdv computes S = Q K^T (one key
+// next product (as in the forward kernels): dK/dV computes S = Q K^T (one key
 // per lane) and dV^T = dO^T P, dK^T = Q^T dS; dq computes S^T = K Q^T (one
 // query per lane) and dQ^T = K^T dS^T.  Tiles sit row-major in LDS with the
 // 16-byte chunk swizzle of attn_common.h; the transposed operands are read
@@ -37,9 +37,6 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-#ifndef ATTN_BWD_AHEAD
-#define ATTN_BWD_AHEAD 3
-#endif
 #ifndef ATTN_BWD_AHEAD_DQ
 #define ATTN_BWD_AHEAD_DQ 1
 #endif
@@ -121,16 +118,22 @@ __device__ inline bf16x8 half_bf16(const f32x16& a, int h) {
 
 // ---------------------------------------------------------------- dK, dV
 
-// Keys stationary: workgroup (b, KV head, 128 keys), wave w owns keys
-// k0 + 32w .. +31 (one per lane of a half-wave pair).  Query tiles of 64 rows
-// of every query head of the group stream through LDS (Q, dO, log2-domain
-// LSE and Delta), double buffered; each tile is worked in two 32-row halves
-// (S and dP, then P and dS, then the dV and dK products), which keeps the
-// score registers of one half live at a time.
+// Keys stationary, two waves per 32 keys: workgroup (b, KV head, 128 keys)
+// of 8 waves, waves w and w+4 (one SIMD) owning keys k0 + 32w .. +31.  Wave w
+// (the S side) computes S = Q K^T, P and dV^T += dO^T P; wave w+4 (the dP
+// side) computes dP = dO V^T and, with P handed over through LDS in fp32,
+// dS = P (dP - Delta) and dK^T += Q^T dS.  Each wave holds one K or V row set
+// and one of the two accumulators, so two waves fit a SIMD; the work and
+// every rounding are fixed, so the results are bitwise reproducible.  Both
+// sides run the same MFMA instructions on different operands; only their
+// vector work differs.  (A one-wave-per-32-keys kernel holding both
+// accumulators needs about 400 registers, so only one wave fits a SIMD; even
+// written out as a software pipeline it ran 2-4 % slower than this pair.)
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf16* __restrict__ dout,
-                                                      const float* __restrict__ delta, const float* __restrict__ lse2,
-                                                      __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
+__global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const __bf16* __restrict__ dout,
+                                                           const float* __restrict__ delta,
+                                                           const float* __restrict__ lse2, __bf16* __restrict__ dk,
+                                                           __bf16* __restrict__ dv) {
   constexpr int BK = 128;        // keys per workgroup
   constexpr int BQ = 64;         // queries per tile
   constexpr int NDC = D / 16;    // contraction chunks over d
@@ -138,23 +141,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf
   constexpr int NQB = BQ / 32;   // 32-query halves of a tile
   using Tile = SwizzledTile<D, BQ>;
   constexpr int TILE = Tile::BYTES;
-  constexpr int BPW = Tile::NBLK / 2;           // blocks per wave: waves 0-1 load Q, 2-3 dO
+  constexpr int BPW = Tile::NBLK / 4;           // blocks per wave: waves 0-3 load Q, 4-7 dO
   constexpr int STAGE = 2 * TILE + 2 * BQ * 4;  // Q, dO, lse2, delta
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  constexpr int PBUF = 64 * 16 * 4;             // one 32 x 32 fp32 P block, 4 KB
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE + 4 * NQB * PBUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(wave);
+  const bool s_side = wu < 4;
+  const int kb = wu & 3;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const float sl2 = p.scale_log2;
 
-  // causal: key tiles in order of decreasing work (a key tile's query range
-  // shrinks as the keys move right), so the light tiles fill the tail
-  // non-causal: XCD-aware, each XCD walks a contiguous range of items, so
-  // the key tiles of one KV head run together and share its Q/dO stream in
-  // that XCD's L2 (the grid is padded to a multiple of 8; padding exits)
   const int ktiles = ceil_div(p.Skv, BK);
   const int nbk = p.B * p.Hkv;
   const int item = CAUSAL ? (int)blockIdx.x : xcd_remap((int)blockIdx.x, nbk * ktiles);
@@ -165,34 +166,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf
   const int kvh = bk - b * p.Hkv;
   const int sq = p.Sq, skv = p.Skv, off = skv - sq;
   const int k0 = kt * BK;
-  const int kw0 = k0 + 32 * wave;
+  const int kw0 = k0 + 32 * kb;
   const int krow = kw0 + l32;
 
-  const __bf16* __restrict__ K = (const __bf16*)p.k + (int64_t)bk * skv * D;
-  const __bf16* __restrict__ V = (const __bf16*)p.v + (int64_t)bk * skv * D;
-
-  // this lane's key row as the B operand of S = Q K^T and dP = dO V^T
-  bf16x8 kf[NDC], vf[NDC];
+  // this lane's K row (S side) or V row (dP side): the B operand
+  const __bf16* __restrict__ KV = (const __bf16*)(s_side ? p.k : p.v) + (int64_t)bk * skv * D;
+  bf16x8 kvf[NDC];
 #pragma unroll
-  for (int c = 0; c < NDC; ++c) {
-    if (krow < skv) {
-      kf[c] = *(const bf16x8*)(K + (int64_t)krow * D + 16 * c + 8 * hh);
-      vf[c] = *(const bf16x8*)(V + (int64_t)krow * D + 16 * c + 8 * hh);
-    } else {
-      kf[c] = bf16x8{};
-      vf[c] = bf16x8{};
-    }
-  }
+  for (int c = 0; c < NDC; ++c)
+    kvf[c] = krow < skv ? *(const bf16x8*)(KV + (int64_t)krow * D + 16 * c + 8 * hh) : bf16x8{};
 
-  f32x16 dkt[NDB], dvt[NDB];  // dK^T, dV^T: rows d, column = this lane's key
+  f32x16 acc[NDB];  // dV^T (S side) or dK^T (dP side): rows d, column = this lane's key
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dkt[db] = f32x16{};
-    dvt[db] = f32x16{};
-  }
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  // queries that can see a key of this workgroup (bottom-right causal):
-  // i >= j - off
   int qbeg = 0;
   if (CAUSAL) {
     qbeg = k0 - off;
@@ -203,32 +190,27 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf
   const int per_head = nqt > qt0 ? nqt - qt0 : 0;
   const int nsteps = per_head * p.group;
 
-  // this wave's HBM -> LDS blocks: tensor (Q or dO) and its byte offsets
-  const bool loads_do = wu >= 2;
   int voff[BPW];
 #pragma unroll
-  for (int i = 0; i < BPW; ++i) voff[i] = Tile::voff((wu & 1) * BPW + i, lane);
+  for (int i = 0; i < BPW; ++i) voff[i] = Tile::voff(kb * BPW + i, lane);
   float lse_reg = 0.0f, del_reg = 0.0f;
   auto step_src = [&](int s, int& h, int& q0) {
     h = kvh * p.group + s / per_head;
     q0 = (qt0 + s % per_head) * BQ;
   };
-  // issue the loads of step s into stage s & 1 (wave 0 also fetches the 64
-  // rows' lse2 and Delta into registers, stored by lstore)
   auto gload = [&](int s) {
     int h, q0;
     step_src(s, h, q0);
     const int64_t row0 = ((int64_t)b * p.H + h) * sq + q0;
     if (wu == 0) {
       const int i = q0 + lane;
-      // rows past the end take part with P = 0
       lse_reg = i < sq ? lse2[row0 + lane] : INFINITY;
       del_reg = i < sq ? delta[row0 + lane] : 0.0f;
     }
     const int nrows = sq - q0 < BQ ? sq - q0 : BQ;
-    const __bf16* src = loads_do ? dout + row0 * D : (const __bf16*)p.q + row0 * D;
+    const __bf16* src = s_side ? (const __bf16*)p.q + row0 * D : dout + row0 * D;
     const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(src, nrows * 2 * D);
-    const unsigned dst = lds_u32(smem) + (s & 1) * STAGE + (loads_do ? TILE : 0) + (wu & 1) * BPW * 1024;
+    const unsigned dst = lds_u32(smem) + (s & 1) * STAGE + (s_side ? 0 : TILE) + kb * BPW * 1024;
 #pragma unroll
     for (int i = 0; i < BPW; ++i) load_lds16(rs, voff[i], 0, dst + i * 1024);
   };
@@ -260,107 +242,67 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Params p, const __bf
     const unsigned char* tdo = tq + TILE;
     const float* tlse = (const float*)(tq + 2 * TILE);
     const float* tdel = tlse + BQ;
-    // Every wave runs every half, also where the causal mask hides all of
-    // it (the first tile of a key block, at most one per query head): the
-    // masked P and dS are 0, and an accumulator updated on every path stays
-    // in one register class (a branch around these MFMAs made the compiler
-    // copy all 128 accumulators between AGPRs and VGPRs every step).
-    //
-    // The step is four MFMA phases of NQK = d/8 MFMAs each:
-    //   A: S and dP of rows 0-31      B: S and dP of rows 32-63
-    //   C: dV and dK of rows 0-31     D: dV and dK of rows 32-63
-    // written out as a software pipeline: MFMA i takes its A operand from a
-    // register ring filled AH MFMAs earlier, and the vector work of rows
-    // 0-31 (mask, P, dS, bf16) is cut into one element per MFMA of B, that
-    // of rows 32-63 into one per MFMA of C, so it runs while the matrix
-    // cores are busy.  sched_barrier fences keep the compiler from
-    // regrouping the slots (left to itself it read each operand one MFMA
-    // ahead and ran the vector work between MFMA blocks: 22 % slower).
-    f32x16 sa[NQB], dp[NQB];
-    bf16x8 pb[NQB][2], sb[NQB][2];
-    {
-      constexpr int NQK = 2 * NDC;
-      constexpr int NM = 4 * NQK;
-      constexpr int AH = ATTN_BWD_AHEAD;
-      constexpr int R = AH + 1;
-      auto fetch = [&](const int i) -> bf16x8 {
-        const int ph = i / NQK, j = i % NQK;
-        if (ph < 2) return frag_rows<D>((j & 1) ? tdo : tq, 32 * ph, j >> 1, l32, hh);
-        const int qc = 2 * (ph - 2) + j / (2 * NDB), db = (j % (2 * NDB)) >> 1;
-        return frag_cols<D>((j & 1) ? tq : tdo, qc, db, tr_row, tr_col);
-      };
-      constexpr int EPS = (16 + NQK - 1) / NQK;  // vector elements per MFMA slot
-      bf16x8 ring[R];
-      f32x4 lv[NQB][4], dl[NQB][4];
-      auto read_stats = [&](const int qb) {
+    // S side: rows of Q for S, columns of dO for dV; dP side: rows of dO
+    // for dP, columns of Q for dK
+    const unsigned char* t_rows = s_side ? tq : tdo;
+    const unsigned char* t_cols = s_side ? tdo : tq;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      float* pbuf = (float*)(smem + 2 * STAGE + (kb * NQB + qb) * PBUF);
+      f32x16 x = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NDC; ++c) x = mfma32(frag_rows<D>(t_rows, 32 * qb, c, l32, hh), kvf[c], x);
+      // query rows 32qb + 8(r/4) + 4hh + r%4 of this lane's key
+      if (s_side) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          lv[qb][g] = *(const f32x4*)(tlse + 32 * qb + 8 * g + 4 * hh);
-          dl[qb][g] = *(const f32x4*)(tdel + 32 * qb + 8 * g + 4 * hh);
-        }
-      };
-      auto vec_elem = [&](const int qb, const int r) {
-        const int g = r >> 2, e = r & 3;
-        float sv = sa[qb][r];
-        if (CAUSAL) sv = krow > q0 + 32 * qb + 8 * g + 4 * hh + e + off ? -INFINITY : sv;
-        const float pv = fast_exp2(fmaf(sv, sl2, -lv[qb][g][e]));
-        sa[qb][r] = pv;
-        dp[qb][r] = pv * (dp[qb][r] - dl[qb][g][e]);
-        if (r == 7 || r == 15) {
-          pb[qb][r >> 3] = half_bf16(sa[qb], r >> 3);
-          sb[qb][r >> 3] = half_bf16(dp[qb], r >> 3);
-        }
-      };
-      static_for<AH>([&](auto ic) { ring[decltype(ic)::value] = fetch(decltype(ic)::value); });
-      sa[0] = sa[1] = dp[0] = dp[1] = f32x16{};
-      static_for<NM>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        constexpr int ph = i / NQK, j = i % NQK;
-        if (i + AH < NM) ring[(i + AH) % R] = fetch(i + AH);
-        // a half's row statistics, two MFMAs before its vector work starts
-        if (ph < 2 && j == NQK - 2) read_stats(ph);
-        const bf16x8 a = ring[i % R];
-        if (ph < 2) {
-          if (j & 1) dp[ph] = mfma32(a, vf[j >> 1], dp[ph]);
-          else sa[ph] = mfma32(a, kf[j >> 1], sa[ph]);
-        } else {
-          const int qb = ph - 2, h2 = j / (2 * NDB), db = (j % (2 * NDB)) >> 1;
-          if (j & 1) dkt[db] = mfma32(a, sb[qb][h2], dkt[db]);
-          else dvt[db] = mfma32(a, pb[qb][h2], dvt[db]);
-        }
-        // EPS elements (of 16) of the previous half's vector work per MFMA
-        if (ph == 1 || ph == 2) {
+          const f32x4 lv = *(const f32x4*)(tlse + 32 * qb + 8 * g + 4 * hh);
 #pragma unroll
-          for (int x = 0; x < EPS; ++x)
-            if (j * EPS + x < 16) vec_elem(ph - 1, j * EPS + x);
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float sv = x[r];
+            if (CAUSAL) sv = krow > q0 + 32 * qb + 8 * g + 4 * hh + e + off ? -INFINITY : sv;
+            x[r] = fast_exp2(fmaf(sv, sl2, -lv[e]));
+          }
+          *(f32x4*)(pbuf + 256 * g + 4 * lane) = f32x4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
         }
-        __builtin_amdgcn_sched_barrier(0);
-      });
+      }
+      __syncthreads();
+      if (!s_side) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 pv = *(const f32x4*)(pbuf + 256 * g + 4 * lane);
+          const f32x4 dl = *(const f32x4*)(tdel + 32 * qb + 8 * g + 4 * hh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * g + e] = pv[e] * (x[4 * g + e] - dl[e]);
+        }
+      }
+      // dV^T += dO^T P (S side), dK^T += Q^T dS (dP side), 16 queries per product
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 xb = half_bf16(x, h2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = mfma32(frag_cols<D>(t_cols, 2 * qb + h2, db, tr_row, tr_col), xb, acc[db]);
+      }
     }
-    // the next stage's loads have landed (its lse2 / Delta are then stored)
-    // before the barrier that publishes it
     __builtin_amdgcn_s_waitcnt(0);
     if (s + 1 < nsteps) lstore(stage ^ 1);
     __syncthreads();
   }
 
-  // dK = s dK^T^T, dV = dV^T^T: this lane's key row, d = 32db + 8rg + 4hh .. +4
+  // dV = dV^T^T (S side), dK = s dK^T^T (dP side): this lane's key row
   if (krow < skv) {
-    __bf16* dkr = dk + ((int64_t)bk * skv + krow) * D;
-    __bf16* dvr = dv + ((int64_t)bk * skv + krow) * D;
-    const float sc = p.scale;
+    __bf16* row = (s_side ? dv : dk) + ((int64_t)bk * skv + krow) * D;
+    const float sc = s_side ? 1.0f : p.scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        bf16x4 wk, wv;
+        bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wk[e] = (__bf16)(dkt[db][4 * rg + e] * sc);
-          wv[e] = (__bf16)(dvt[db][4 * rg + e]);
-        }
-        *(bf16x4*)(dkr + 32 * db + 8 * rg + 4 * hh) = wk;
-        *(bf16x4*)(dvr + 32 * db + 8 * rg + 4 * hh) = wv;
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][4 * rg + e] * sc);
+        *(bf16x4*)(row + 32 * db + 8 * rg + 4 * hh) = w;
       }
   }
 }
@@ -487,7 +429,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
     // skip the tiles no row of this wave sees (causal); a branch around the
     // whole step, so the accumulators stay where they are
     if (k0 < w_end) {
-      // Four MFMA phases, the same software pipeline as the dK/dV kernel:
+      // Four MFMA phases written out as a software pipeline (sched_barrier
+      // fences; left to itself the compiler read each operand one MFMA
+      // ahead and ran the vector work between MFMA blocks):
       //   A: S^T and dP^T of keys 0-31    B: S^T and dP^T of keys 32-63
       //   C: dQ^T from keys 0-31          D: dQ^T from keys 32-63
       // with the vector work (mask, P, dS, bf16) of keys 0-31 spread over
@@ -581,10 +525,11 @@ hipError_t launch_bwd_d(const Params& p, const __bf16* dout, float* delta, float
   if (p.Skv > 0) {
     const long g1 = p.causal ? (long)p.B * p.Hkv * ceil_div(p.Skv, 128) : pad8((long)p.B * p.Hkv * ceil_div(p.Skv, 128));
     if (p.causal)
-      hipLaunchKernelGGL((dkdv_kernel<D, true>), dim3((unsigned)g1), dim3(256), 0, st, p, dout, delta, lse2, dk, dv);
-    else
-      hipLaunchKernelGGL((dkdv_kernel<D, false>), dim3((unsigned)g1), dim3(256), 0, st, p, dout, delta, lse2, dk,
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, true>), dim3((unsigned)g1), dim3(512), 0, st, p, dout, delta, lse2, dk,
                          dv);
+    else
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, false>), dim3((unsigned)g1), dim3(512), 0, st, p, dout, delta, lse2,
+                         dk, dv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
