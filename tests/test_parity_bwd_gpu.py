@@ -112,6 +112,24 @@ def test_backward_long_sequence_two_heads(causal):
     compare(tuple(g[:, heads] for g in got), want, f"4K causal={causal} heads {heads}")
 
 
+def test_backward_gqa_long_sequence_one_group():
+    """4K tokens, 32 query heads on 8 KV heads, causal; the oracle checks one
+    KV head's group in full (its dK and dV sum the four query heads)."""
+    B, H, Hkv, S, d = 1, 32, 8, 4096, 128
+    say("backward GQA 4K causal")
+    q = synth.normal_tensor(8300, (B, H, S, d), "bf16")
+    k = synth.normal_tensor(8301, (B, Hkv, S, d), "bf16")
+    v = synth.normal_tensor(8302, (B, Hkv, S, d), "bf16")
+    do = synth.normal_tensor(8303, (B, H, S, d), "bf16")
+    got = run(q, k, v, do, True)
+    kvh = 5
+    heads = list(range(kvh * (H // Hkv), (kvh + 1) * (H // Hkv)))
+    want = bwd_oracle.attention_backward(host_f32(q, "bf16")[:, heads], host_f32(k, "bf16")[:, [kvh]],
+                                         host_f32(v, "bf16")[:, [kvh]], host_f32(do, "bf16")[:, heads],
+                                         1.0 / math.sqrt(d), True)
+    compare((got[0][:, heads], got[1][:, [kvh]], got[2][:, [kvh]]), want, f"GQA 4K KV head {kvh}")
+
+
 def test_backward_no_keys_and_bitwise_repeatable():
     import exact_attention_09_amd as ea
     say("backward: no keys, repeatability")
