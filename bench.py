@@ -117,12 +117,14 @@ def run_workload(name: str, steps: int, warmup: int, inputs=None):
                               stream=stream.cuda_stream)
     elif wl.backward:
         dout = to_device(x["dout"], wl.dtype)
-        ea.attn_fwd(q, k, v, o, lse, causal=wl.causal, scale=wl.scale)   # o, lse of the forward, untimed
+        # o, lse of the forward, untimed
+        ea.attn_fwd(q, k, v, o, lse, causal=wl.causal, scale=wl.scale, cu_seqlens=cu)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        bws = torch.empty(ea.attn_bwd_workspace_bytes(wl.B, wl.H, wl.Sq), dtype=torch.uint8, device="cuda")
+        bws = torch.empty(ea.attn_bwd_workspace_bytes(1 if wl.varlen else wl.B, wl.H, wl.Sq), dtype=torch.uint8,
+                          device="cuda")
 
         def step():
-            ea.attn_bwd(q, k, v, o, lse, dout, causal=wl.causal, scale=wl.scale, dq=dq, dk=dk, dv=dv,
+            ea.attn_bwd(q, k, v, o, lse, dout, causal=wl.causal, scale=wl.scale, cu_seqlens=cu, dq=dq, dk=dk, dv=dv,
                         workspace=bws, stream=stream.cuda_stream)
     elif wl.window > 0 or wl.sinks:
         sk = torch.from_numpy(x["sinks"]).cuda() if wl.sinks else None
@@ -234,7 +236,7 @@ def main(argv=None):
     if not args.quick:
         for name in ("mha_causal_s8192_d128", "mha_causal_s2048_d64", "varlen_gqa_causal_d128",
                      "swa_sink_s32768_d128", "decode_gqa_s16384_d128", "decode_paged_gqa_s16384_d128",
-                     "bwd_mha_s8192_d128", "bwd_mha_causal_s8192_d128"):
+                     "bwd_mha_s8192_d128", "bwd_mha_causal_s8192_d128", "bwd_varlen_gqa_causal_d128"):
             print(f"# timing {name}", file=sys.stderr, flush=True)
             w, ns, tt = run_workload(name, args.steps, args.warmup)
             entry = {"ms_per_step": round(tt["wall_ms_per_step"], 4), "launch_ms_mean": round(tt["event_ms_mean"], 4)}

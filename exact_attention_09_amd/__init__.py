@@ -15,7 +15,8 @@ Names mirror the C entry points:
   per-head attention sinks;
 * ``attn_fwd_layout`` is the general bf16 call: BHSD or BSHD (packed THD for
   varlen) tensors, plus the window and sinks;
-* ``attn_bwd`` computes dq, dk, dv from the forward's o and lse;
+* ``attn_bwd`` computes dq, dk, dv from the forward's o and lse (dense or
+  packed varlen);
 * ``attn_fwd_paged`` runs split-KV decode over a paged KV cache (block
   table and per-sequence key counts) and returns ``(o, lse)``;
 * ``attn_workspace_bytes``, ``attn_decode_num_splits``,
@@ -83,7 +84,7 @@ def load_library(path: str = LIB_PATH):
         ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(AttnOpts)]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 6 + [
-        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(AttnOpts)]
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(AttnOpts)]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 3
     lib.attn_workspace_bytes.restype = ctypes.c_size_t
@@ -334,14 +335,15 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, o=None, lse=None
     return o, lse
 
 
-def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = None, dq=None, dk=None,
-             dv=None, stream=None, workspace=None):
+def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = None, cu_seqlens=None,
+             dq=None, dk=None, dv=None, stream=None, workspace=None):
     """Gradients through ``attn_bwd``: q [B,H,Sq,d], k/v [B,Hkv,Skv,d], the
-    forward's o and lse, and dout [B,H,Sq,d] (bf16 on the GPU).  Returns
-    ``(dq, dk, dv)``."""
+    forward's o and lse, and dout [B,H,Sq,d] (bf16 on the GPU); with
+    ``cu_seqlens`` (int32 on the GPU) the packed varlen layout of
+    ``attn_fwd_ex``.  Returns ``(dq, dk, dv)``."""
     import torch
     lib = load_library()
-    B, H, Hkv, Sq, Skv, d, dk_ = _shapes(q, k, None)
+    B, H, Hkv, Sq, Skv, d, dk_ = _shapes(q, k, cu_seqlens)
     if dk_ != d or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape) \
             or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != tuple(q.shape[:-1]):
         raise ValueError("shapes: q, o, dout [B,H,Sq,d]; k, v [B,Hkv,Skv,d]; lse [B,H,Sq]")
@@ -359,8 +361,11 @@ def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None
         stream = torch.cuda.current_stream(q.device).cuda_stream
     opts = AttnOpts(0, workspace.data_ptr() if workspace is not None else None,
                     workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise ValueError("cu_seqlens must be an int32 tensor on the GPU")
     st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                      B, H, Hkv, Sq, Skv, d, float(scale), int(bool(causal)), ctypes.c_void_p(stream),
+                      B, H, Hkv, Sq, Skv, d, float(scale), int(bool(causal)),
+                      _ptr(cu_seqlens) if cu_seqlens is not None else None, ctypes.c_void_p(stream),
                       ctypes.byref(opts))
     if st != ATTN_OK:
         raise AttnError(st, attn_last_error())

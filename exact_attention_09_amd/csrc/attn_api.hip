@@ -366,7 +366,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Sq) {
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                      void* dq, void* dk, void* dv, int B, int H, int Hkv, int Sq, int Skv, int d, float scale,
-                     int causal, void* stream, const attn_opts* opts) {
+                     int causal, const int32_t* cu_seqlens, void* stream, const attn_opts* opts) {
   g_err[0] = '\0';
   // ---- validation: no HIP call until every check has passed
   if (B < 0 || H < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || d < 0)
@@ -384,14 +384,20 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return fail(ATTN_EINVAL, "q, k, v, o, dout, dq, dk, dv must be 16-byte aligned");
   if (!aligned(lse, 4)) return fail(ATTN_EINVAL, "lse must be 4-byte aligned");
-  const long double q_elems = (long double)B * H * Sq * d;
-  const long double kv_elems = (long double)B * Hkv * Skv * d;
+  const bool varlen = cu_seqlens != nullptr;
+  if (varlen) {
+    if (Sq != Skv) return fail(ATTN_EINVAL, "varlen needs Sq == Skv == total tokens (got %d, %d)", Sq, Skv);
+    if (!aligned(cu_seqlens, 4)) return fail(ATTN_EINVAL, "cu_seqlens must be 4-byte aligned");
+  }
+  const long double q_elems = (long double)(varlen ? 1 : B) * H * Sq * d;
+  const long double kv_elems = (long double)(varlen ? 1 : B) * Hkv * Skv * d;
   if (q_elems > 9.0e18L || kv_elems > 9.0e18L) return fail(ATTN_EINVAL, "tensor too large");
-  if ((long)B * H * attn::ceil_div(Sq, 128) > 0x7ffffff0L || (long)B * Hkv * attn::ceil_div(Skv, 128) > 0x7ffffff0L)
-    return fail(ATTN_EINVAL, "too many tiles");
+  const long q_tiles = varlen ? (long)H * (Sq / 128 + B) : (long)B * H * attn::ceil_div(Sq, 128);
+  const long k_tiles = varlen ? (long)Hkv * (Skv / 128 + B) : (long)B * Hkv * attn::ceil_div(Skv, 128);
+  if (q_tiles > 0x7ffffff0L || k_tiles > 0x7ffffff0L) return fail(ATTN_EINVAL, "too many tiles");
 
   attn::Params p{};
-  p.q = q; p.k = k; p.v = v; p.o = (void*)o; p.lse = (float*)lse;
+  p.q = q; p.k = k; p.v = v; p.o = (void*)o; p.lse = (float*)lse; p.cu = cu_seqlens;
   p.B = B; p.H = H; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv; p.d = d;
   p.group = H / Hkv;
   p.causal = causal ? 1 : 0;
@@ -401,7 +407,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   p.kv_rs = d;
   hipStream_t st = (hipStream_t)stream;
 
-  if (Sq == 0) {
+  if (Sq == 0) {  // dense only: a varlen call with no token returned above
     // no query: dK = dV = 0
     attn::Params z = p;
     z.B = 1; z.H = 1; z.Sq = (int)((long)B * Hkv * Skv); z.cu = nullptr; z.lse = nullptr; z.sinks = nullptr;
@@ -413,7 +419,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
     }
     return e == hipSuccess ? ATTN_OK : hip_fail(e, "fill kernel");
   }
-  const size_t need = attn_bwd_workspace_bytes(B, H, Sq);
+  const size_t need = attn_bwd_workspace_bytes(varlen ? 1 : B, H, Sq);
   void* ws = nullptr;
   bool own = false;
   if (opts != nullptr && opts->workspace != nullptr) {

@@ -116,6 +116,29 @@ __device__ inline bf16x8 half_bf16(const f32x16& a, int h) {
   return to_bf16x8(a[rb + 0], a[rb + 1], a[rb + 2], a[rb + 3], a[rb + 4], a[rb + 5], a[rb + 6], a[rb + 7]);
 }
 
+// Varlen: the per-head tile index vt of packed sequences with `tile`-row
+// tiles (tiles of one sequence consecutive, sequences in order); sets the
+// sequence's first row s0, its length and the tile within it.  False past
+// the last tile.  Sequence bounds are clamped into [0, T].
+__device__ inline bool varlen_tile(const Params& p, int vt, int tile, int& s0, int& len, int& t_in) {
+  const int T = p.Sq;
+  int acc = 0;
+  for (int bb = 0; bb < p.B; ++bb) {
+    int a = p.cu[bb], e = p.cu[bb + 1];
+    a = a < 0 ? 0 : (a > T ? T : a);
+    e = e < a ? a : (e > T ? T : e);
+    const int nt = ceil_div(e - a, tile);
+    if (vt < acc + nt) {
+      s0 = a;
+      len = e - a;
+      t_in = vt - acc;
+      return true;
+    }
+    acc += nt;
+  }
+  return false;
+}
+
 // ---------------------------------------------------------------- dK, dV
 
 // Keys stationary, two waves per 32 keys: workgroup (b, KV head, 128 keys)
@@ -129,7 +152,7 @@ __device__ inline bf16x8 half_bf16(const f32x16& a, int h) {
 // vector work differs.  (A one-wave-per-32-keys kernel holding both
 // accumulators needs about 400 registers, so only one wave fits a SIMD; even
 // written out as a software pipeline it ran 2-4 % slower than this pair.)
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const __bf16* __restrict__ dout,
                                                            const float* __restrict__ delta,
                                                            const float* __restrict__ lse2, __bf16* __restrict__ dk,
@@ -156,21 +179,46 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
   const int hh = lane >> 5;
   const float sl2 = p.scale_log2;
 
-  const int ktiles = ceil_div(p.Skv, BK);
-  const int nbk = p.B * p.Hkv;
-  const int item = CAUSAL ? (int)blockIdx.x : xcd_remap((int)blockIdx.x, nbk * ktiles);
-  if (item < 0) return;
-  const int kt = CAUSAL ? item / nbk : item % ktiles;
-  const int bk = CAUSAL ? item - kt * nbk : item / ktiles;  // b * Hkv + kvh
-  const int b = bk / p.Hkv;
-  const int kvh = bk - b * p.Hkv;
-  const int sq = p.Sq, skv = p.Skv, off = skv - sq;
+  // the item: (b, kv head, key tile); dense causal: key tiles in order of
+  // decreasing work (a key tile's query range shrinks as the keys move
+  // right), non-causal: XCD-aware (the key tiles of a KV head share its
+  // Q/dO stream in one L2; the grid is padded to a multiple of 8); varlen:
+  // (kv head, tile of the packed sequences), located through cu_seqlens.
+  int kt, b, kvh, sq, skv;
+  int64_t kv_row0, q_head_rows;  // row of this sequence's key 0; rows per query head (varlen: T)
+  int64_t q_row_shift;           // varlen: the sequence's first row
+  if constexpr (VARLEN) {
+    const int ktu = p.tiles_per_head;
+    kvh = (int)blockIdx.x / ktu;
+    int s0, len;
+    if (!varlen_tile(p, (int)blockIdx.x - kvh * ktu, BK, s0, len, kt)) return;
+    b = 0;
+    sq = skv = len;
+    kv_row0 = (int64_t)kvh * p.Sq + s0;
+    q_head_rows = p.Sq;
+    q_row_shift = s0;
+  } else {
+    const int ktiles = ceil_div(p.Skv, BK);
+    const int nbk = p.B * p.Hkv;
+    const int item = CAUSAL ? (int)blockIdx.x : xcd_remap((int)blockIdx.x, nbk * ktiles);
+    if (item < 0) return;
+    kt = CAUSAL ? item / nbk : item % ktiles;
+    const int bk = CAUSAL ? item - kt * nbk : item / ktiles;  // b * Hkv + kvh
+    b = bk / p.Hkv;
+    kvh = bk - b * p.Hkv;
+    sq = p.Sq;
+    skv = p.Skv;
+    kv_row0 = (int64_t)bk * skv;
+    q_head_rows = sq;
+    q_row_shift = 0;
+  }
+  const int off = skv - sq;
   const int k0 = kt * BK;
   const int kw0 = k0 + 32 * kb;
   const int krow = kw0 + l32;
 
   // this lane's K row (S side) or V row (dP side): the B operand
-  const __bf16* __restrict__ KV = (const __bf16*)(s_side ? p.k : p.v) + (int64_t)bk * skv * D;
+  const __bf16* __restrict__ KV = (const __bf16*)(s_side ? p.k : p.v) + kv_row0 * D;
   bf16x8 kvf[NDC];
 #pragma unroll
   for (int c = 0; c < NDC; ++c)
@@ -201,7 +249,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
   auto gload = [&](int s) {
     int h, q0;
     step_src(s, h, q0);
-    const int64_t row0 = ((int64_t)b * p.H + h) * sq + q0;
+    const int64_t row0 = ((int64_t)b * p.H + h) * q_head_rows + q_row_shift + q0;
     if (wu == 0) {
       const int i = q0 + lane;
       lse_reg = i < sq ? lse2[row0 + lane] : INFINITY;
@@ -293,7 +341,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
 
   // dV = dV^T^T (S side), dK = s dK^T^T (dP side): this lane's key row
   if (krow < skv) {
-    __bf16* row = (s_side ? dv : dk) + ((int64_t)bk * skv + krow) * D;
+    __bf16* row = (s_side ? dv : dk) + (kv_row0 + krow) * D;
     const float sc = s_side ? 1.0f : p.scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -313,7 +361,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
 // queries q0 + 32w .. +31 (one per lane of a half-wave pair); key tiles of 64
 // rows stream through LDS, double buffered, each worked in two 32-key
 // halves.  Two workgroups share a CU.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16* __restrict__ dout,
                                                     const float* __restrict__ delta, const float* __restrict__ lse2,
                                                     __bf16* __restrict__ dq) {
@@ -335,27 +383,42 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
   const int hh = lane >> 5;
   const float sl2 = p.scale_log2;
 
-  // causal: query tiles in order of decreasing work (the last tiles see the
-  // most keys)
-  // non-causal: XCD-aware as in the dK/dV kernel (the query tiles of a head
-  // share its K/V stream in one L2)
-  const int qtiles = ceil_div(p.Sq, BMQ);
-  const int nbh = p.B * p.H;
-  const int item = CAUSAL ? (int)blockIdx.x : xcd_remap((int)blockIdx.x, nbh * qtiles);
-  if (item < 0) return;
-  const int bh = CAUSAL ? item % nbh : item / qtiles;
-  const int tile = CAUSAL ? qtiles - 1 - item / nbh : item - bh * qtiles;
-  const int b = bh / p.H;
-  const int h = bh - b * p.H;
-  const int sq = p.Sq, skv = p.Skv, off = skv - sq;
+  // the item: (b, query head, query tile); dense causal: query tiles in
+  // order of decreasing work (the last tiles see the most keys), non-causal:
+  // XCD-aware as in the dK/dV kernel (the query tiles of a head share its
+  // K/V stream in one L2); varlen: (query head, tile of the packed
+  // sequences), located through cu_seqlens.
+  int tile, sq, skv;
+  int64_t row0, kv0;  // this head's (sequence's) query row 0 and key row 0
+  if constexpr (VARLEN) {
+    const int qtu = p.tiles_per_head;
+    const int h = (int)blockIdx.x / qtu;
+    int s0, len;
+    if (!varlen_tile(p, (int)blockIdx.x - h * qtu, BMQ, s0, len, tile)) return;
+    sq = skv = len;
+    row0 = (int64_t)h * p.Sq + s0;
+    kv0 = (int64_t)(h / p.group) * p.Sq + s0;
+  } else {
+    const int qtiles = ceil_div(p.Sq, BMQ);
+    const int nbh = p.B * p.H;
+    const int item = CAUSAL ? (int)blockIdx.x : xcd_remap((int)blockIdx.x, nbh * qtiles);
+    if (item < 0) return;
+    const int bh = CAUSAL ? item % nbh : item / qtiles;
+    tile = CAUSAL ? qtiles - 1 - item / nbh : item - bh * qtiles;
+    const int b = bh / p.H;
+    const int h = bh - b * p.H;
+    sq = p.Sq;
+    skv = p.Skv;
+    row0 = (int64_t)bh * sq;
+    kv0 = ((int64_t)b * p.Hkv + h / p.group) * skv;
+  }
+  const int off = skv - sq;
   const int q0 = tile * BMQ;
   const int qw0 = q0 + 32 * wave;
   const int qrow = qw0 + l32;
-  const int64_t row0 = (int64_t)bh * sq;
 
   const __bf16* __restrict__ Q = (const __bf16*)p.q + row0 * D;
   const __bf16* __restrict__ dO = dout + row0 * D;
-  const int64_t kv0 = ((int64_t)b * p.Hkv + h / p.group) * skv;
   const __bf16* __restrict__ K = (const __bf16*)p.k + kv0 * D;
   const __bf16* __restrict__ V = (const __bf16*)p.v + kv0 * D;
 
@@ -511,34 +574,59 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
   }
 }
 
+template <int D, bool VARLEN>
+hipError_t launch_tiles(const Params& p, const __bf16* dout, float* delta, float* lse2, __bf16* dq, __bf16* dk,
+                        __bf16* dv, hipStream_t st) {
+  // dense non-causal grids are padded to a multiple of 8 for the XCD
+  // mapping; varlen grids cover an upper bound of the tiles per head
+  // (T / tile + sequences), the surplus items exit at once
+  auto pad8 = [](long n) { return (n + 7) / 8 * 8; };
+  Params q = p;
+  if (p.Skv > 0) {
+    long g1;
+    if (VARLEN) {
+      q.tiles_per_head = p.Sq / 128 + p.B;
+      g1 = (long)p.Hkv * q.tiles_per_head;
+    } else {
+      g1 = (long)p.B * p.Hkv * ceil_div(p.Skv, 128);
+      if (!p.causal) g1 = pad8(g1);
+    }
+    if (p.causal)
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, true, VARLEN>), dim3((unsigned)g1), dim3(512), 0, st, q, dout, delta,
+                         lse2, dk, dv);
+    else
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, false, VARLEN>), dim3((unsigned)g1), dim3(512), 0, st, q, dout, delta,
+                         lse2, dk, dv);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  long g2;
+  if (VARLEN) {
+    q.tiles_per_head = p.Sq / 128 + p.B;
+    g2 = (long)p.H * q.tiles_per_head;
+  } else {
+    g2 = (long)p.B * p.H * ceil_div(p.Sq, 128);
+    if (!p.causal) g2 = pad8(g2);
+  }
+  if (p.causal)
+    hipLaunchKernelGGL((dq_kernel<D, true, VARLEN>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta, lse2, dq);
+  else
+    hipLaunchKernelGGL((dq_kernel<D, false, VARLEN>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta, lse2, dq);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_bwd_d(const Params& p, const __bf16* dout, float* delta, float* lse2, __bf16* dq, __bf16* dk,
                         __bf16* dv, hipStream_t st) {
-  const long rows = (long)p.B * p.H * p.Sq;
+  const bool var = p.cu != nullptr;
+  const long rows = (long)(var ? 1 : p.B) * p.H * p.Sq;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
                      (const __bf16*)p.o, dout, p.lse, delta, lse2, rows);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // non-causal grids are padded to a multiple of 8 for the XCD mapping
-  auto pad8 = [](long n) { return (n + 7) / 8 * 8; };
-  if (p.Skv > 0) {
-    const long g1 = p.causal ? (long)p.B * p.Hkv * ceil_div(p.Skv, 128) : pad8((long)p.B * p.Hkv * ceil_div(p.Skv, 128));
-    if (p.causal)
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, true>), dim3((unsigned)g1), dim3(512), 0, st, p, dout, delta, lse2, dk,
-                         dv);
-    else
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, false>), dim3((unsigned)g1), dim3(512), 0, st, p, dout, delta, lse2,
-                         dk, dv);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const long g2 = p.causal ? (long)p.B * p.H * ceil_div(p.Sq, 128) : pad8((long)p.B * p.H * ceil_div(p.Sq, 128));
-  if (p.causal)
-    hipLaunchKernelGGL((dq_kernel<D, true>), dim3((unsigned)g2), dim3(256), 0, st, p, dout, delta, lse2, dq);
-  else
-    hipLaunchKernelGGL((dq_kernel<D, false>), dim3((unsigned)g2), dim3(256), 0, st, p, dout, delta, lse2, dq);
-  return hipGetLastError();
+  return var ? launch_tiles<D, true>(p, dout, delta, lse2, dq, dk, dv, st)
+             : launch_tiles<D, false>(p, dout, delta, lse2, dq, dk, dv, st);
 }
 
 }  // namespace

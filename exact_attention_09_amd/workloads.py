@@ -183,6 +183,10 @@ WORKLOADS = {
                                    dtype="bf16", causal=False, backward=True),
     "bwd_mha_causal_s8192_d128": Workload("bwd_mha_causal_s8192_d128", 9, B=1, H=32, Hkv=32, Sq=8192, Skv=8192,
                                           d=128, dtype="bf16", causal=True, backward=True),
+    # the backward of the varlen prefill's packing (8 sequences, 22342 tokens)
+    "bwd_varlen_gqa_causal_d128": Workload("bwd_varlen_gqa_causal_d128", 10, B=len(VARLEN_LENGTHS), H=32, Hkv=8,
+                                           Sq=sum(VARLEN_LENGTHS), Skv=sum(VARLEN_LENGTHS), d=128, dtype="bf16",
+                                           causal=True, lengths=VARLEN_LENGTHS, backward=True),
     # the same decode over a paged cache: 16-token pages (the CUDA course's
     # typical block size) scattered by a seeded permutation
     "decode_paged_gqa_s16384_d128": Workload("decode_paged_gqa_s16384_d128", 6, B=32, H=32, Hkv=8, Sq=1,

@@ -188,26 +188,31 @@ attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cac
                            const attn_opts* opts);
 
 /* Backward pass: gradients of attn_fwd's output with respect to q, k, v
- * (bf16, BHSD, dense; causal or not).  The pages name the backward only as
- * the tutorial's section 5.4 Ascend example (dQ partial tiles added with bf16
- * atomics, with the resulting error); this library computes the derivative of
- * the forward's definition without atomics, bitwise reproducibly:
+ * (bf16, BHSD, causal or not, dense or packed variable-length sequences).
+ * The pages name the backward only as the tutorial's section 5.4 Ascend
+ * example (dQ partial tiles added with bf16 atomics, with the resulting
+ * error); this library computes the derivative of the forward's definition
+ * without atomics, bitwise reproducibly:
  *   Delta_i = rowsum(dout_i * o_i),  P = exp(scale q k^T - LSE)
  *   dv = P^T dout,  dS = P * (dout v^T - Delta),  dq = scale dS k,
  *   dk = scale dS^T q
  * with the grouped-query sums over each KV head's query heads.
  *   q, o, dout, dq : [B, H, Sq, d] bf16       lse : [B, H, Sq] fp32 (attn_fwd's)
  *   k, v, dk, dv   : [B, Hkv, Skv, d] bf16
- * o and lse must be the forward outputs for the same q, k, v, scale and
- * causal flag.  P and dS are rounded to bf16 (nearest even) for the products
- * that use them; all sums are fp32.  The workspace (opts, may be NULL) holds
- * Delta and the LSE in log2 units, one fp32 per query row each:
- * attn_bwd_workspace_bytes(B, H, Sq) bytes, 256-byte aligned, else it is
- * allocated stream-ordered.  Validation, errors and ordering on `stream`
- * as for attn_fwd_ex; opts->num_splits is ignored. */
+ * cu_seqlens != NULL selects varlen exactly as in attn_fwd_ex: B sequences
+ * packed into [1, H, T, d] (q, o, dout, dq), [1, Hkv, T, d] (k, v, dk, dv)
+ * and [1, H, T] (lse), Sq == Skv == T == cu_seqlens[B], each sequence
+ * attending to itself (causal offset 0).
+ * o and lse must be the forward outputs for the same q, k, v, scale,
+ * causal flag and cu_seqlens.  P and dS are rounded to bf16 (nearest even)
+ * for the products that use them; all sums are fp32.  The workspace (opts,
+ * may be NULL) holds Delta and the LSE in log2 units, one fp32 per query row
+ * each: attn_bwd_workspace_bytes(B, H, Sq) bytes (varlen: (1, H, T)),
+ * 256-byte aligned, else it is allocated stream-ordered.  Validation, errors
+ * and ordering on `stream` as for attn_fwd_ex; opts->num_splits is ignored. */
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                      void* dq, void* dk, void* dv, int B, int H, int Hkv, int Sq, int Skv, int d, float scale,
-                     int causal, void* stream, const attn_opts* opts);
+                     int causal, const int32_t* cu_seqlens, void* stream, const attn_opts* opts);
 
 /* Bytes of workspace attn_bwd needs (0 for invalid sizes). */
 size_t attn_bwd_workspace_bytes(int B, int H, int Sq);

@@ -196,8 +196,8 @@ def test_layout_empty_problem_is_a_no_op(lib):
 
 
 def bwd_call(lib, *, q=P, k=P, v=P, o=P, do=P, lse=P, dq=Q2, dk=Q2, dv=Q2, B=1, H=4, Hkv=2, Sq=8, Skv=8, d=128,
-             scale=0.1, causal=0, opts=None):
-    return lib.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, Hkv, Sq, Skv, d, scale, causal, None,
+             scale=0.1, causal=0, cu=None, opts=None):
+    return lib.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, Hkv, Sq, Skv, d, scale, causal, cu, None,
                         ctypes.byref(opts) if opts is not None else None)
 
 
@@ -213,6 +213,9 @@ def bwd_call(lib, *, q=P, k=P, v=P, o=P, do=P, lse=P, dq=Q2, dk=Q2, dv=Q2, B=1, 
     (dict(lse=ctypes.c_void_p(0x100002)), ea.ATTN_EINVAL),
     (dict(Sq=-1), ea.ATTN_EINVAL),
     (dict(opts=ea.AttnOpts(0, 0x500000, 16)), ea.ATTN_EINVAL),
+    # varlen: q and k hold the same tokens; cu_seqlens aligned
+    (dict(cu=ctypes.c_void_p(0x400000), Sq=8, Skv=9), ea.ATTN_EINVAL),
+    (dict(cu=ctypes.c_void_p(0x400002)), ea.ATTN_EINVAL),
 ])
 def test_bwd_rejects_before_any_hip_call(lib, kw, status):
     assert bwd_call(lib, **kw) == status

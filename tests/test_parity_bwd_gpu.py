@@ -130,6 +130,49 @@ def test_backward_gqa_long_sequence_one_group():
     compare((got[0][:, heads], got[1][:, [kvh]], got[2][:, [kvh]]), want, f"GQA 4K KV head {kvh}")
 
 
+def run_varlen(q, k, v, do, lengths, causal):
+    import exact_attention_09_amd as ea
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), device="cuda")
+    qt, kt, vt, dot = (to_device(x, "bf16") for x in (q, k, v, do))
+    o, lse = ea.attn_fwd_ex(qt, kt, vt, causal=causal, cu_seqlens=cu)
+    dq, dk, dv = ea.attn_bwd(qt, kt, vt, o, lse, dot, causal=causal, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    return tuple(x.float().cpu().numpy().astype(np.float64) for x in (dq, dk, dv))
+
+
+VARLEN_CASES = [
+    # (sequence lengths, H, Hkv, d, causal)
+    ((1, 130, 77, 300, 64, 129), 4, 2, 64, True),
+    ((257, 1, 128, 500), 4, 4, 128, False),
+    ((200, 333, 1000, 64), 8, 2, 128, True),
+    ((0, 96, 0, 129), 2, 1, 128, True),    # empty sequences in the list
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: "-".join(map(str, c[0])) + f"-{c[1]}-{c[2]}-{c[3]}-{c[4]}")
+def test_backward_varlen(case):
+    """Packed sequences: each sequence's gradients equal the fp64 oracle's
+    for that sequence alone (the varlen layout is per-sequence dense
+    attention, each sequence attending to itself)."""
+    lengths, H, Hkv, d, causal = case
+    say(f"backward varlen {case}")
+    T = sum(lengths)
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    q = synth.normal_tensor(seed * 10 + 0, (1, H, T, d), "bf16")
+    k = synth.normal_tensor(seed * 10 + 1, (1, Hkv, T, d), "bf16")
+    v = synth.normal_tensor(seed * 10 + 2, (1, Hkv, T, d), "bf16")
+    do = synth.normal_tensor(seed * 10 + 3, (1, H, T, d), "bf16")
+    got = run_varlen(q, k, v, do, lengths, causal)
+    s0 = 0
+    for i, n in enumerate(lengths):
+        if n > 0:
+            sl = slice(s0, s0 + n)
+            want = bwd_oracle.attention_backward(*(host_f32(x, "bf16")[:, :, sl] for x in (q, k, v, do)),
+                                                 1.0 / math.sqrt(d), causal)
+            compare(tuple(g[:, :, sl] for g in got), want, f"varlen {case} sequence {i}")
+        s0 += n
+
+
 def test_backward_no_keys_and_bitwise_repeatable():
     import exact_attention_09_amd as ea
     say("backward: no keys, repeatability")
@@ -153,14 +196,31 @@ def test_backward_no_keys_and_bitwise_repeatable():
 
 @pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.backward])
 def test_backward_workload(name):
-    """The timed backward workloads at their full size (32 heads of 8K
-    tokens, as timed); the oracle checks one head in full (MHA, so heads are
-    independent)."""
+    """The timed backward workloads at their full size, on the inputs bench.py
+    times.  Dense (32 heads of 8K tokens): the oracle checks one head in full
+    (MHA, so heads are independent).  Varlen (8 packed sequences, 22342
+    tokens, 32 query heads on 8 KV heads): the oracle checks one KV head's
+    group on the shortest and the longest sequence."""
     wl = WORKLOADS[name]
     say(f"backward workload {name}")
     x = wl.make_inputs()
-    got = run(x["q"], x["k"], x["v"], x["dout"], wl.causal)
-    heads = [wl.H - 3]
-    want = bwd_oracle.attention_backward(*(host_f32(x[n], wl.dtype)[:, heads] for n in ("q", "k", "v", "dout")),
-                                         wl.scale, wl.causal)
-    compare(tuple(g[:, heads] for g in got), want, f"{name} head {heads}")
+    if not wl.varlen:
+        got = run(x["q"], x["k"], x["v"], x["dout"], wl.causal)
+        heads = [wl.H - 3]
+        want = bwd_oracle.attention_backward(*(host_f32(x[n], wl.dtype)[:, heads] for n in ("q", "k", "v", "dout")),
+                                             wl.scale, wl.causal)
+        compare(tuple(g[:, heads] for g in got), want, f"{name} head {heads}")
+        return
+    lengths = tuple(int(n) for n in wl.lengths)
+    got = run_varlen(x["q"], x["k"], x["v"], x["dout"], lengths, wl.causal)
+    starts = np.concatenate([[0], np.cumsum(lengths)])
+    kvh = 3
+    group = wl.H // wl.Hkv
+    heads = list(range(kvh * group, (kvh + 1) * group))
+    qf, kf, vf, dof = (host_f32(x[n], wl.dtype) for n in ("q", "k", "v", "dout"))
+    for i in (int(np.argmin(lengths)), int(np.argmax(lengths))):
+        sl = slice(int(starts[i]), int(starts[i + 1]))
+        want = bwd_oracle.attention_backward(qf[:, heads, sl], kf[:, [kvh], sl], vf[:, [kvh], sl], dof[:, heads, sl],
+                                             wl.scale, wl.causal)
+        compare((got[0][:, heads, sl], got[1][:, [kvh], sl], got[2][:, [kvh], sl]), want,
+                f"{name} sequence {i} (length {lengths[i]}) KV head {kvh}")
