@@ -139,6 +139,65 @@ __device__ inline bool varlen_tile(const Params& p, int vt, int tile, int& s0, i
   return false;
 }
 
+// Varlen, causal: the items listed by work, heaviest first.  An item of
+// level r costs about r tile-pairs: key tile k of a sequence of n tiles has
+// level n - k (it sees the query tiles k .. n-1), query tile t level t + 1.
+// Levels run from the largest n down to 1; within a level, sequences in
+// order.  F(r) = sum_i max(0, n_i - r + 1) items have level >= r, so item f
+// has the level r with F(r+1) <= f < F(r) (binary search), and is the
+// (f - F(r+1))-th sequence with n_i >= r.  Sets s0, len and the level; false
+// past the last item.  Costs a few scans of cu_seqlens per workgroup, so it
+// is used for short sequence lists only.
+constexpr int kRankedSeqs = 64;
+__device__ inline bool varlen_ranked(const Params& p, int f, int tile, int& s0, int& len, int& level) {
+  const int T = p.Sq;
+  auto bounds = [&](int bb, int& a, int& e) {
+    a = p.cu[bb];
+    e = p.cu[bb + 1];
+    a = a < 0 ? 0 : (a > T ? T : a);
+    e = e < a ? a : (e > T ? T : e);
+  };
+  auto items_from = [&](int r) {  // F(r)
+    int acc = 0;
+    for (int bb = 0; bb < p.B; ++bb) {
+      int a, e;
+      bounds(bb, a, e);
+      const int n = ceil_div(e - a, tile) - r + 1;
+      acc += n > 0 ? n : 0;
+    }
+    return acc;
+  };
+  int nmax = 0;
+  for (int bb = 0; bb < p.B; ++bb) {
+    int a, e;
+    bounds(bb, a, e);
+    const int n = ceil_div(e - a, tile);
+    nmax = n > nmax ? n : nmax;
+  }
+  if (nmax == 0 || f >= items_from(1)) return false;
+  int lo = 1, hi = nmax;  // the largest r with F(r) > f
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (items_from(mid) > f) {
+      lo = mid;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  level = lo;
+  int j = f - items_from(lo + 1);
+  for (int bb = 0; bb < p.B; ++bb) {
+    int a, e;
+    bounds(bb, a, e);
+    if (ceil_div(e - a, tile) >= level && j-- == 0) {
+      s0 = a;
+      len = e - a;
+      return true;
+    }
+  }
+  return false;
+}
+
 // ---------------------------------------------------------------- dK, dV
 
 // Keys stationary, two waves per 32 keys: workgroup (b, KV head, 128 keys)
@@ -189,9 +248,17 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
   int64_t q_row_shift;           // varlen: the sequence's first row
   if constexpr (VARLEN) {
     const int ktu = p.tiles_per_head;
-    kvh = (int)blockIdx.x / ktu;
     int s0, len;
-    if (!varlen_tile(p, (int)blockIdx.x - kvh * ktu, BK, s0, len, kt)) return;
+    if (CAUSAL && p.B <= kRankedSeqs) {
+      // heaviest first over all KV heads: the heads interleaved
+      kvh = (int)blockIdx.x % p.Hkv;
+      int level;
+      if (!varlen_ranked(p, (int)blockIdx.x / p.Hkv, BK, s0, len, level)) return;
+      kt = ceil_div(len, BK) - level;
+    } else {
+      kvh = (int)blockIdx.x / ktu;
+      if (!varlen_tile(p, (int)blockIdx.x - kvh * ktu, BK, s0, len, kt)) return;
+    }
     b = 0;
     sq = skv = len;
     kv_row0 = (int64_t)kvh * p.Sq + s0;
@@ -392,9 +459,17 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
   int64_t row0, kv0;  // this head's (sequence's) query row 0 and key row 0
   if constexpr (VARLEN) {
     const int qtu = p.tiles_per_head;
-    const int h = (int)blockIdx.x / qtu;
-    int s0, len;
-    if (!varlen_tile(p, (int)blockIdx.x - h * qtu, BMQ, s0, len, tile)) return;
+    int h, s0, len;
+    if (CAUSAL && p.B <= kRankedSeqs) {
+      // heaviest first over all query heads: the heads interleaved
+      h = (int)blockIdx.x % p.H;
+      int level;
+      if (!varlen_ranked(p, (int)blockIdx.x / p.H, BMQ, s0, len, level)) return;
+      tile = level - 1;
+    } else {
+      h = (int)blockIdx.x / qtu;
+      if (!varlen_tile(p, (int)blockIdx.x - h * qtu, BMQ, s0, len, tile)) return;
+    }
     sq = skv = len;
     row0 = (int64_t)h * p.Sq + s0;
     kv0 = (int64_t)(h / p.group) * p.Sq + s0;
