@@ -117,15 +117,26 @@ def run_workload(name: str, steps: int, warmup: int, inputs=None):
                               stream=stream.cuda_stream)
     elif wl.backward:
         dout = to_device(x["dout"], wl.dtype)
-        # o, lse of the forward, untimed
-        ea.attn_fwd(q, k, v, o, lse, causal=wl.causal, scale=wl.scale, cu_seqlens=cu)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         bws = torch.empty(ea.attn_bwd_workspace_bytes(1 if wl.varlen else wl.B, wl.H, wl.Sq), dtype=torch.uint8,
                           device="cuda")
+        if wl.window > 0 or wl.sinks:
+            sk = torch.from_numpy(x["sinks"]).cuda() if wl.sinks else None
+            ds = torch.empty(wl.H, dtype=torch.float32, device="cuda") if wl.sinks else None
+            # o, lse of the forward, untimed
+            ea.attn_fwd_window_sink(q, k, v, o, lse, window=wl.window, sinks=sk, scale=wl.scale, cu_seqlens=cu)
 
-        def step():
-            ea.attn_bwd(q, k, v, o, lse, dout, causal=wl.causal, scale=wl.scale, cu_seqlens=cu, dq=dq, dk=dk, dv=dv,
-                        workspace=bws, stream=stream.cuda_stream)
+            def step():
+                ea.attn_bwd_window_sink(q, k, v, o, lse, dout, window=wl.window, sinks=sk, scale=wl.scale,
+                                        cu_seqlens=cu, dq=dq, dk=dk, dv=dv, dsinks=ds, workspace=bws,
+                                        stream=stream.cuda_stream)
+        else:
+            # o, lse of the forward, untimed
+            ea.attn_fwd(q, k, v, o, lse, causal=wl.causal, scale=wl.scale, cu_seqlens=cu)
+
+            def step():
+                ea.attn_bwd(q, k, v, o, lse, dout, causal=wl.causal, scale=wl.scale, cu_seqlens=cu, dq=dq, dk=dk,
+                            dv=dv, workspace=bws, stream=stream.cuda_stream)
     elif wl.window > 0 or wl.sinks:
         sk = torch.from_numpy(x["sinks"]).cuda() if wl.sinks else None
 
@@ -236,7 +247,8 @@ def main(argv=None):
     if not args.quick:
         for name in ("mha_causal_s8192_d128", "mha_causal_s2048_d64", "varlen_gqa_causal_d128",
                      "swa_sink_s32768_d128", "decode_gqa_s16384_d128", "decode_paged_gqa_s16384_d128",
-                     "bwd_mha_s8192_d128", "bwd_mha_causal_s8192_d128", "bwd_varlen_gqa_causal_d128"):
+                     "bwd_mha_s8192_d128", "bwd_mha_causal_s8192_d128", "bwd_varlen_gqa_causal_d128",
+                     "bwd_swa_sink_s8192_d128"):
             print(f"# timing {name}", file=sys.stderr, flush=True)
             w, ns, tt = run_workload(name, args.steps, args.warmup)
             entry = {"ms_per_step": round(tt["wall_ms_per_step"], 4), "launch_ms_mean": round(tt["event_ms_mean"], 4)}

@@ -16,7 +16,8 @@ Names mirror the C entry points:
 * ``attn_fwd_layout`` is the general bf16 call: BHSD or BSHD (packed THD for
   varlen) tensors, plus the window and sinks;
 * ``attn_bwd`` computes dq, dk, dv from the forward's o and lse (dense or
-  packed varlen);
+  packed varlen), ``attn_bwd_window_sink`` the same for the window/sink
+  forward (plus the sink gradients);
 * ``attn_fwd_paged`` runs split-KV decode over a paged KV cache (block
   table and per-sequence key counts) and returns ``(o, lse)``;
 * ``attn_workspace_bytes``, ``attn_decode_num_splits``,
@@ -37,7 +38,7 @@ ATTN_BHSD, ATTN_BSHD = 0, 1
 ATTN_MAX_SPLITS = 256
 
 EXPORTED = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_window_sink", "attn_fwd_layout",
-            "attn_fwd_paged", "attn_bwd", "attn_bwd_workspace_bytes", "attn_workspace_bytes",
+            "attn_fwd_paged", "attn_bwd", "attn_bwd_window_sink", "attn_bwd_workspace_bytes", "attn_workspace_bytes",
             "attn_decode_num_splits", "attn_status_string", "attn_last_error")
 
 
@@ -85,6 +86,9 @@ def load_library(path: str = LIB_PATH):
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(AttnOpts)]
+    lib.attn_bwd_window_sink.restype = ctypes.c_int
+    lib.attn_bwd_window_sink.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(AttnOpts)]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 3
     lib.attn_workspace_bytes.restype = ctypes.c_size_t
@@ -370,6 +374,47 @@ def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None
     if st != ATTN_OK:
         raise AttnError(st, attn_last_error())
     return dq, dk, dv
+
+
+def attn_bwd_window_sink(q, k, v, o, lse, dout, *, window: int = 0, sinks=None, scale: float | None = None,
+                         cu_seqlens=None, dq=None, dk=None, dv=None, dsinks=None, stream=None, workspace=None):
+    """Gradients of ``attn_fwd_window_sink`` (causal, sliding ``window``,
+    per-head ``sinks`` fp32 [H]) through ``attn_bwd_window_sink``; shapes as
+    for ``attn_bwd``.  Returns ``(dq, dk, dv, dsinks)`` (``dsinks`` None
+    without sinks)."""
+    import torch
+    lib = load_library()
+    B, H, Hkv, Sq, Skv, d, dk_ = _shapes(q, k, cu_seqlens)
+    if dk_ != d or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape) \
+            or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != tuple(q.shape[:-1]):
+        raise ValueError("shapes: q, o, dout [B,H,Sq,d]; k, v [B,Hkv,Skv,d]; lse [B,H,Sq]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor on the GPU")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 tensor on the GPU")
+    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_cuda or sinks.numel() != H):
+        raise ValueError("sinks must be a float32 tensor of H values on the GPU")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise ValueError("cu_seqlens must be an int32 tensor on the GPU")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if sinks is not None and dsinks is None:
+        dsinks = torch.empty(H, dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    opts = AttnOpts(0, workspace.data_ptr() if workspace is not None else None,
+                    workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    st = lib.attn_bwd_window_sink(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(dsinks) if sinks is not None else None, B, H, Hkv, Sq, Skv, d,
+                                  float(scale), _ptr(cu_seqlens), int(window), _ptr(sinks), ctypes.c_void_p(stream),
+                                  ctypes.byref(opts))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_last_error())
+    return dq, dk, dv, (dsinks if sinks is not None else None)
 
 
 def attn_bwd_workspace_bytes(B: int, H: int, Sq: int) -> int:

@@ -364,11 +364,21 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Sq) {
   return 2 * (((size_t)B * H * Sq * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign);
 }
 
-attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+}  // extern "C"
+
+namespace {
+
+// The backward behind attn_bwd and attn_bwd_window_sink: window > 0 and
+// sinks != NULL are causal (the caller validated that).
+attn_status backward(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                      void* dq, void* dk, void* dv, int B, int H, int Hkv, int Sq, int Skv, int d, float scale,
-                     int causal, const int32_t* cu_seqlens, void* stream, const attn_opts* opts) {
+                     int causal, const int32_t* cu_seqlens, int window, const float* sinks, float* dsinks,
+                     void* stream, const attn_opts* opts) {
   g_err[0] = '\0';
   // ---- validation: no HIP call until every check has passed
+  if (window < 0) return fail(ATTN_EINVAL, "window must be >= 0 (got %d)", window);
+  if (sinks != nullptr && (!aligned(sinks, 4) || dsinks == nullptr || !aligned(dsinks, 4)))
+    return fail(ATTN_EINVAL, "sinks need a 4-byte aligned dsinks output of H floats");
   if (B < 0 || H < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || d < 0)
     return fail(ATTN_EINVAL, "negative size (B=%d H=%d Hkv=%d Sq=%d Skv=%d d=%d)", B, H, Hkv, Sq, Skv, d);
   if (B == 0 || H == 0 || (Sq == 0 && Skv == 0)) return ATTN_OK;
@@ -401,6 +411,8 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   p.B = B; p.H = H; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv; p.d = d;
   p.group = H / Hkv;
   p.causal = causal ? 1 : 0;
+  p.window = window;
+  p.sinks = sinks;
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.q_rs = d;
@@ -416,6 +428,12 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
     if (e == hipSuccess) {
       z.o = dv;
       e = attn::launch_fill_empty(z, true, st);
+    }
+    if (e == hipSuccess && sinks != nullptr) {  // dsinks = 0: H fp32 zeros through the same fill kernel
+      z.Sq = 1;
+      z.d = H;
+      z.o = dsinks;
+      e = attn::launch_fill_empty(z, false, st);
     }
     return e == hipSuccess ? ATTN_OK : hip_fail(e, "fill kernel");
   }
@@ -438,13 +456,32 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   attn_status status = ATTN_OK;
   float* delta = (float*)ws;
   float* lse2 = (float*)((char*)ws + need / 2);
-  hipError_t e = attn::launch_backward(p, dout, delta, lse2, dq, dk, dv, st);
+  hipError_t e = attn::launch_backward(p, dout, delta, lse2, dq, dk, dv, dsinks, st);
   if (e != hipSuccess) status = hip_fail(e, "backward kernels");
   if (own) {
     const hipError_t ef = hipFreeAsync(ws, st);
     if (ef != hipSuccess && status == ATTN_OK) status = hip_fail(ef, "workspace release");
   }
   return status;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, int B, int H, int Hkv, int Sq, int Skv, int d, float scale,
+                     int causal, const int32_t* cu_seqlens, void* stream, const attn_opts* opts) {
+  return backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Sq, Skv, d, scale, causal, cu_seqlens, 0, nullptr,
+                  nullptr, stream, opts);
+}
+
+attn_status attn_bwd_window_sink(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                 const float* lse, void* dq, void* dk, void* dv, float* dsinks, int B, int H, int Hkv,
+                                 int Sq, int Skv, int d, float scale, const int32_t* cu_seqlens, int window,
+                                 const float* sinks, void* stream, const attn_opts* opts) {
+  return backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Sq, Skv, d, scale, 1, cu_seqlens, window, sinks,
+                  dsinks, stream, opts);
 }
 
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,

@@ -70,6 +70,31 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
   }
 }
 
+// dsink_h = -sum over the rows of head h of P_sink,i Delta_i, with
+// P_sink,i = exp(sink_h - LSE_i) (the forward's LSE counts the sink; a row
+// that saw no key has LSE = sink and Delta = 0).  One workgroup per head;
+// each thread sums a fixed stride of rows, then a fixed tree: bitwise
+// reproducible.
+__global__ __launch_bounds__(256) void dsink_kernel(const float* __restrict__ sinks, const float* __restrict__ delta,
+                                                    const float* __restrict__ lse2, float* __restrict__ dsinks, int nb,
+                                                    int H, int S) {
+  __shared__ float part[256];
+  const int h = blockIdx.x;
+  const float sk = sinks[h] * kLog2e;
+  float acc = 0.0f;
+  for (int b = 0; b < nb; ++b) {
+    const int64_t row0 = ((int64_t)b * H + h) * S;
+    for (int i = threadIdx.x; i < S; i += 256) acc += fast_exp2(sk - lse2[row0 + i]) * delta[row0 + i];
+  }
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int m = 128; m >= 1; m >>= 1) {
+    if ((int)threadIdx.x < m) part[threadIdx.x] += part[threadIdx.x + m];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dsinks[h] = -part[0];
+}
+
 // ---------------------------------------------------------------- shared
 
 // A row-major tile of `ROWS` rows of D bf16 in LDS, 16-byte chunks swizzled
@@ -211,7 +236,7 @@ __device__ inline bool varlen_ranked(const Params& p, int f, int tile, int& s0, 
 // vector work differs.  (A one-wave-per-32-keys kernel holding both
 // accumulators needs about 400 registers, so only one wave fits a SIMD; even
 // written out as a software pipeline it ran 2-4 % slower than this pair.)
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool LOCAL>
 __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const __bf16* __restrict__ dout,
                                                            const float* __restrict__ delta,
                                                            const float* __restrict__ lse2, __bf16* __restrict__ dk,
@@ -295,13 +320,21 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
+  // queries that see a key of this workgroup: i >= j - off (causal) and,
+  // under a window W, i < j - off + W
+  const int W = LOCAL ? p.window : 0;
   int qbeg = 0;
   if (CAUSAL) {
     qbeg = k0 - off;
     qbeg = qbeg < 0 ? 0 : qbeg;
   }
+  int qend = sq;
+  if (W > 0) {
+    const long e = (long)k0 + BK - 1 - off + W;
+    qend = e < 0 ? 0 : (e < sq ? (int)e : sq);
+  }
   const int qt0 = qbeg / BQ;
-  const int nqt = ceil_div(sq, BQ);
+  const int nqt = ceil_div(qend, BQ);
   const int per_head = nqt > qt0 ? nqt - qt0 : 0;
   const int nsteps = per_head * p.group;
 
@@ -376,7 +409,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
             float sv = x[r];
-            if (CAUSAL) sv = krow > q0 + 32 * qb + 8 * g + 4 * hh + e + off ? -INFINITY : sv;
+            const int i_off = q0 + 32 * qb + 8 * g + 4 * hh + e + off;  // query row + off
+            if (CAUSAL) sv = krow > i_off ? -INFINITY : sv;
+            if (LOCAL && W > 0) sv = krow <= i_off - W ? -INFINITY : sv;
             x[r] = fast_exp2(fmaf(sv, sl2, -lv[e]));
           }
           *(f32x4*)(pbuf + 256 * g + 4 * lane) = f32x4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
@@ -428,7 +463,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
 // queries q0 + 32w .. +31 (one per lane of a half-wave pair); key tiles of 64
 // rows stream through LDS, double buffered, each worked in two 32-key
 // halves.  Two workgroups share a CU.
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool LOCAL>
 __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16* __restrict__ dout,
                                                     const float* __restrict__ delta, const float* __restrict__ lse2,
                                                     __bf16* __restrict__ dq) {
@@ -518,10 +553,20 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
   const int q_hi = q0 + BMQ < sq ? q0 + BMQ : sq;
   const int kv_end = CAUSAL ? causal_kv_end(q_hi, off, skv) : skv;
   const int nt = ceil_div(kv_end, BN);
-  int w_end = 0;
+  // under a window W row i sees keys from i + off - W + 1: the workgroup
+  // starts at the tile of its top row's first key, each wave skips the
+  // tiles before its own
+  const int W = LOCAL ? p.window : 0;
+  auto win_lo = [&](const int i) {
+    const long b = (long)i + off - W + 1;
+    return b < 0 ? 0 : (b > skv ? skv : (int)b);
+  };
+  const int t_first = W > 0 ? (win_lo(q0) < kv_end ? win_lo(q0) : kv_end) / BN : 0;
+  int w_end = 0, w_lo = 0;
   if (qw0 < sq) {
     const int w_hi = qw0 + 32 < sq ? qw0 + 32 : sq;
     w_end = CAUSAL ? causal_kv_end(w_hi, off, skv) : skv;
+    if (W > 0) w_lo = win_lo(qw0);
   }
 
   const bool loads_v = wu >= 2;
@@ -546,7 +591,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqt[db] = f32x16{};
 
-  if (nt > 0) gload(0);
+  if (t_first < nt) gload(t_first);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -555,18 +600,20 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
     const int c_lim = qrow + off + 1;
     lim = c_lim < lim ? c_lim : lim;
   }
-  // keys < lim are visible; compared as lim - 4hh against a wave-uniform key
+  // keys < lim (and >= lo under a window) are visible; compared as lim - 4hh
+  // and lo - 4hh against a wave-uniform key
   const int lim_h = lim - 4 * hh;
+  const int lo_h = (W > 0 ? qrow + off - W + 1 : -(1 << 30)) - 4 * hh;
 
-  for (int t = 0; t < nt; ++t) {
+  for (int t = t_first; t < nt; ++t) {
     const int stage = t & 1;
     const int k0 = t * BN;
     if (t + 1 < nt) gload(t + 1);
     const unsigned char* tk = smem + stage * 2 * TILE;
     const unsigned char* tv = tk + TILE;
-    // skip the tiles no row of this wave sees (causal); a branch around the
-    // whole step, so the accumulators stay where they are
-    if (k0 < w_end) {
+    // skip the tiles no row of this wave sees (causal, window); a branch
+    // around the whole step, so the accumulators stay where they are
+    if (k0 < w_end && k0 + BN > w_lo) {
       // Four MFMA phases written out as a software pipeline (sched_barrier
       // fences; left to itself the compiler read each operand one MFMA
       // ahead and ran the vector work between MFMA blocks):
@@ -598,7 +645,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
       // key k0 + 32kbi + 8(r/4) + 4hh + r%4 of this lane's query
       auto vec_elem = [&](const int kbi, const int r) {
         float sv = st[kbi][r];
-        if (CAUSAL) sv = k0 + 32 * kbi + 8 * (r >> 2) + (r & 3) >= lim_h ? -INFINITY : sv;
+        const int kk = k0 + 32 * kbi + 8 * (r >> 2) + (r & 3);
+        if (CAUSAL) sv = kk >= lim_h ? -INFINITY : sv;
+        if (LOCAL) sv = kk < lo_h ? -INFINITY : sv;
         const float pv = fast_exp2(fmaf(sv, sl2, neg_lse));
         dpt[kbi][r] = pv * (dpt[kbi][r] - del);
         if (r == 7 || r == 15) sb[kbi][r >> 3] = half_bf16(dpt[kbi], r >> 3);
@@ -649,12 +698,13 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
   }
 }
 
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool LOCAL>
 hipError_t launch_tiles(const Params& p, const __bf16* dout, float* delta, float* lse2, __bf16* dq, __bf16* dk,
                         __bf16* dv, hipStream_t st) {
   // dense non-causal grids are padded to a multiple of 8 for the XCD
   // mapping; varlen grids cover an upper bound of the tiles per head
-  // (T / tile + sequences), the surplus items exit at once
+  // (T / tile + sequences), the surplus items exit at once.  LOCAL (a
+  // sliding window) is causal.
   auto pad8 = [](long n) { return (n + 7) / 8 * 8; };
   Params q = p;
   if (p.Skv > 0) {
@@ -666,12 +716,15 @@ hipError_t launch_tiles(const Params& p, const __bf16* dout, float* delta, float
       g1 = (long)p.B * p.Hkv * ceil_div(p.Skv, 128);
       if (!p.causal) g1 = pad8(g1);
     }
-    if (p.causal)
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, true, VARLEN>), dim3((unsigned)g1), dim3(512), 0, st, q, dout, delta,
-                         lse2, dk, dv);
+    if (LOCAL)
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, true, VARLEN, true>), dim3((unsigned)g1), dim3(512), 0, st, q, dout,
+                         delta, lse2, dk, dv);
+    else if (p.causal)
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, true, VARLEN, false>), dim3((unsigned)g1), dim3(512), 0, st, q, dout,
+                         delta, lse2, dk, dv);
     else
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, false, VARLEN>), dim3((unsigned)g1), dim3(512), 0, st, q, dout, delta,
-                         lse2, dk, dv);
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, false, VARLEN, false>), dim3((unsigned)g1), dim3(512), 0, st, q, dout,
+                         delta, lse2, dk, dv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -683,36 +736,52 @@ hipError_t launch_tiles(const Params& p, const __bf16* dout, float* delta, float
     g2 = (long)p.B * p.H * ceil_div(p.Sq, 128);
     if (!p.causal) g2 = pad8(g2);
   }
-  if (p.causal)
-    hipLaunchKernelGGL((dq_kernel<D, true, VARLEN>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta, lse2, dq);
+  if (LOCAL)
+    hipLaunchKernelGGL((dq_kernel<D, true, VARLEN, true>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta, lse2,
+                       dq);
+  else if (p.causal)
+    hipLaunchKernelGGL((dq_kernel<D, true, VARLEN, false>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta,
+                       lse2, dq);
   else
-    hipLaunchKernelGGL((dq_kernel<D, false, VARLEN>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta, lse2, dq);
+    hipLaunchKernelGGL((dq_kernel<D, false, VARLEN, false>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta,
+                       lse2, dq);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_bwd_d(const Params& p, const __bf16* dout, float* delta, float* lse2, __bf16* dq, __bf16* dk,
-                        __bf16* dv, hipStream_t st) {
+                        __bf16* dv, float* dsinks, hipStream_t st) {
   const bool var = p.cu != nullptr;
-  const long rows = (long)(var ? 1 : p.B) * p.H * p.Sq;
+  const int nb = var ? 1 : p.B;
+  const long rows = (long)nb * p.H * p.Sq;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
                      (const __bf16*)p.o, dout, p.lse, delta, lse2, rows);
-  const hipError_t e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return var ? launch_tiles<D, true>(p, dout, delta, lse2, dq, dk, dv, st)
-             : launch_tiles<D, false>(p, dout, delta, lse2, dq, dk, dv, st);
+  if (p.sinks != nullptr) {
+    hipLaunchKernelGGL(dsink_kernel, dim3((unsigned)p.H), dim3(256), 0, st, p.sinks, (const float*)delta,
+                       (const float*)lse2, dsinks, nb, p.H, p.Sq);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const bool local = p.window > 0;
+  if (var)
+    return local ? launch_tiles<D, true, true>(p, dout, delta, lse2, dq, dk, dv, st)
+                 : launch_tiles<D, true, false>(p, dout, delta, lse2, dq, dk, dv, st);
+  return local ? launch_tiles<D, false, true>(p, dout, delta, lse2, dq, dk, dv, st)
+               : launch_tiles<D, false, false>(p, dout, delta, lse2, dq, dk, dv, st);
 }
 
 }  // namespace
 
 hipError_t launch_backward(const Params& p, const void* dout, float* delta, float* lse2, void* dq, void* dk,
-                           void* dv, hipStream_t st) {
+                           void* dv, float* dsinks, hipStream_t st) {
   if ((long)p.B * p.H * p.Sq <= 0) return hipSuccess;
   if (p.d == 128)
-    return launch_bwd_d<128>(p, (const __bf16*)dout, delta, lse2, (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, st);
+    return launch_bwd_d<128>(p, (const __bf16*)dout, delta, lse2, (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, dsinks, st);
   if (p.d == 64)
-    return launch_bwd_d<64>(p, (const __bf16*)dout, delta, lse2, (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, st);
+    return launch_bwd_d<64>(p, (const __bf16*)dout, delta, lse2, (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, dsinks, st);
   return hipErrorInvalidValue;
 }
 

@@ -28,9 +28,11 @@ hipError_t launch_combine(const Params& p, bool out_bf16, hipStream_t st);
 // Rows that can see no key at all (Skv == 0): O = 0, LSE = -inf.
 hipError_t launch_fill_empty(const Params& p, bool out_bf16, hipStream_t st);
 
-// Backward pass (bf16, BHSD, dense): Delta and the log2-domain LSE into
-// `delta` and `lse2` (B*H*Sq floats each), then dK and dV, then dQ.
+// Backward pass (bf16, BHSD, dense or varlen; p.window > 0: sliding window,
+// p.sinks != null: sink gradients into dsinks [H]): Delta and the
+// log2-domain LSE into `delta` and `lse2` (one float per query row each),
+// then dK and dV, then dQ.
 hipError_t launch_backward(const Params& p, const void* dout, float* delta, float* lse2, void* dq, void* dk,
-                           void* dv, hipStream_t st);
+                           void* dv, float* dsinks, hipStream_t st);
 
 }  // namespace attn

@@ -183,6 +183,10 @@ WORKLOADS = {
                                    dtype="bf16", causal=False, backward=True),
     "bwd_mha_causal_s8192_d128": Workload("bwd_mha_causal_s8192_d128", 9, B=1, H=32, Hkv=32, Sq=8192, Skv=8192,
                                           d=128, dtype="bf16", causal=True, backward=True),
+    # the backward of causal attention with a 2048-token window and per-head
+    # sinks over 8K tokens (MHA, so that one head's full oracle checks it)
+    "bwd_swa_sink_s8192_d128": Workload("bwd_swa_sink_s8192_d128", 11, B=1, H=32, Hkv=32, Sq=8192, Skv=8192,
+                                        d=128, dtype="bf16", causal=True, window=2048, sinks=True, backward=True),
     # the backward of the varlen prefill's packing (8 sequences, 22342 tokens)
     "bwd_varlen_gqa_causal_d128": Workload("bwd_varlen_gqa_causal_d128", 10, B=len(VARLEN_LENGTHS), H=32, Hkv=8,
                                            Sq=sum(VARLEN_LENGTHS), Skv=sum(VARLEN_LENGTHS), d=128, dtype="bf16",

@@ -214,6 +214,24 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* dq, void* dk, void* dv, int B, int H, int Hkv, int Sq, int Skv, int d, float scale,
                      int causal, const int32_t* cu_seqlens, void* stream, const attn_opts* opts);
 
+/* Backward pass of attn_fwd_window_sink: causal attention with a sliding
+ * window (window > 0; 0 = none) and/or per-head attention sinks (sinks: fp32
+ * [H] logits, may be NULL), dense or varlen, as attn_bwd otherwise.  The
+ * tutorial's sections 5.2 (the window band) and 4.6-4.7 (the sink: a logit in
+ * each row's softmax without a value) define the forward; its derivative
+ * changes only the mask for the window, while each sink is one more softmax
+ * column whose gradient is
+ *   dsinks[h] = - sum over the rows i of head h of exp(sink_h - LSE_i) Delta_i
+ * (o and lse must be attn_fwd_window_sink's for the same window and sinks; a
+ * row that saw no key has LSE = sink and contributes 0).  dsinks: fp32 [H]
+ * output, required when sinks != NULL, summed in a fixed order (bitwise
+ * reproducible).  Workspace, validation, errors and ordering as for
+ * attn_bwd. */
+attn_status attn_bwd_window_sink(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                 const float* lse, void* dq, void* dk, void* dv, float* dsinks, int B, int H, int Hkv,
+                                 int Sq, int Skv, int d, float scale, const int32_t* cu_seqlens, int window,
+                                 const float* sinks, void* stream, const attn_opts* opts);
+
 /* Bytes of workspace attn_bwd needs (0 for invalid sizes). */
 size_t attn_bwd_workspace_bytes(int B, int H, int Sq);
 

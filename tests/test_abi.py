@@ -222,6 +222,31 @@ def test_bwd_rejects_before_any_hip_call(lib, kw, status):
     assert ea.attn_last_error() != ""
 
 
+def bwd_ws_call(lib, *, q=P, k=P, v=P, o=P, do=P, lse=P, dq=Q2, dk=Q2, dv=Q2, ds=Q2, B=1, H=4, Hkv=2, Sq=8, Skv=8,
+                d=128, scale=0.1, cu=None, window=4, sinks=P, opts=None):
+    return lib.attn_bwd_window_sink(q, k, v, o, do, lse, dq, dk, dv, ds, B, H, Hkv, Sq, Skv, d, scale, cu, window,
+                                    sinks, None, ctypes.byref(opts) if opts is not None else None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=-1), ea.ATTN_EINVAL),
+    (dict(ds=None), ea.ATTN_EINVAL),                       # sinks without dsinks
+    (dict(ds=ctypes.c_void_p(0x200002)), ea.ATTN_EINVAL),
+    (dict(sinks=ctypes.c_void_p(0x600002)), ea.ATTN_EINVAL),
+    (dict(q=None), ea.ATTN_EINVAL),
+    (dict(d=96), ea.ATTN_EUNSUPPORTED),
+    (dict(cu=ctypes.c_void_p(0x400000), Sq=8, Skv=9), ea.ATTN_EINVAL),
+])
+def test_bwd_window_sink_rejects_before_any_hip_call(lib, kw, status):
+    assert bwd_ws_call(lib, **kw) == status
+    assert ea.attn_last_error() != ""
+
+
+def test_bwd_window_sink_empty_problem_is_a_no_op(lib):
+    assert bwd_ws_call(lib, B=0) == ea.ATTN_OK
+    assert bwd_ws_call(lib, Sq=0, Skv=0, sinks=None, ds=None) == ea.ATTN_OK
+
+
 def test_bwd_empty_and_workspace(lib):
     assert bwd_call(lib, B=0) == ea.ATTN_OK
     assert bwd_call(lib, Sq=0, Skv=0) == ea.ATTN_OK

@@ -173,6 +173,64 @@ def test_backward_varlen(case):
         s0 += n
 
 
+def run_window_sink(q, k, v, do, window, sinks):
+    import exact_attention_09_amd as ea
+    qt, kt, vt, dot = (to_device(x, "bf16") for x in (q, k, v, do))
+    st = torch.from_numpy(np.asarray(sinks, np.float32)).cuda() if sinks is not None else None
+    o, lse = ea.attn_fwd_window_sink(qt, kt, vt, window=window, sinks=st)
+    dq, dk, dv, ds = ea.attn_bwd_window_sink(qt, kt, vt, o, lse, dot, window=window, sinks=st)
+    torch.cuda.synchronize()
+    grads = tuple(x.float().cpu().numpy().astype(np.float64) for x in (dq, dk, dv))
+    return grads, (ds.cpu().numpy().astype(np.float64) if ds is not None else None)
+
+
+def compare_dsinks(got, q, k, v, do, window, sinks, heads, what):
+    """dsink_h = -sum_i P_sink,i Delta_i: against the oracle's, within 1e-2 of
+    sum_i |P_sink,i Delta_i| (the terms may cancel, so their magnitudes, from
+    the fp64 forward oracle, set the scale)."""
+    import oracle
+    d = q.shape[-1]
+    o, lse = oracle.attention(*(host_f32(x, "bf16") for x in (q, k, v)), 1.0 / math.sqrt(d), True,
+                              window=window, sinks=np.asarray(sinks, np.float32))
+    delta = (o * host_f32(do, "bf16").astype(np.float64)).sum(-1)          # [B, H, Sq]
+    psink = np.exp(np.asarray(sinks, np.float64)[None, :, None] - lse)       # [B, H, Sq]
+    want = -(psink * delta).sum(axis=(0, 2))
+    mag = np.abs(psink * delta).sum(axis=(0, 2))
+    for h in heads:
+        err = abs(got[h] - want[h])
+        say(f"  {what}: dsink[{h}] {got[h]:.6g} vs {want[h]:.6g} (|terms| {mag[h]:.3g}, err {err:.3g})")
+        assert err <= 1e-2 * mag[h] + 1e-6, f"{what}: dsink[{h}] error {err:.3g}"
+
+
+WS_CASES = [
+    # (B, H, Hkv, Sq, Skv, d, window, with_sinks)
+    (1, 4, 2, 300, 300, 128, 64, True),
+    (2, 4, 4, 257, 257, 64, 100, False),
+    (1, 4, 1, 200, 333, 128, 50, True),     # Sq < Skv
+    (1, 2, 2, 300, 130, 128, 40, True),     # Sq > Skv: rows with no key (LSE = sink)
+    (1, 8, 2, 512, 512, 128, 0, True),      # sinks only
+    (1, 4, 4, 600, 600, 64, 1000, True),    # window longer than the keys
+]
+
+
+@pytest.mark.parametrize("case", WS_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_backward_window_sink(case):
+    B, H, Hkv, Sq, Skv, d, w, with_sinks = case
+    say(f"backward window/sink {case}")
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    q = synth.normal_tensor(seed * 10 + 0, (B, H, Sq, d), "bf16")
+    k = synth.normal_tensor(seed * 10 + 1, (B, Hkv, Skv, d), "bf16")
+    v = synth.normal_tensor(seed * 10 + 2, (B, Hkv, Skv, d), "bf16")
+    do = synth.normal_tensor(seed * 10 + 3, (B, H, Sq, d), "bf16")
+    sinks = synth.normal_tensor(seed * 10 + 5, (H,), "f32") * np.float32(2.0) if with_sinks else None
+    got, ds = run_window_sink(q, k, v, do, w, sinks)
+    want = bwd_oracle.attention_backward(*(host_f32(x, "bf16") for x in (q, k, v, do)), 1.0 / math.sqrt(d), True,
+                                         window=w, sinks=sinks)
+    compare(got, want[:3], str(case))
+    if with_sinks:
+        compare_dsinks(ds, q, k, v, do, w, sinks, range(H), str(case))
+
+
 def test_backward_no_keys_and_bitwise_repeatable():
     import exact_attention_09_amd as ea
     say("backward: no keys, repeatability")
@@ -204,6 +262,19 @@ def test_backward_workload(name):
     wl = WORKLOADS[name]
     say(f"backward workload {name}")
     x = wl.make_inputs()
+    if wl.window > 0 or wl.sinks:
+        # window/sink (MHA): one head in full, and its sink gradient
+        got, ds = run_window_sink(x["q"], x["k"], x["v"], x["dout"], wl.window, x["sinks"] if wl.sinks else None)
+        h = wl.H - 3
+        sl = (slice(None), [h])
+        want = bwd_oracle.attention_backward(*(host_f32(x[n], wl.dtype)[sl] for n in ("q", "k", "v", "dout")),
+                                             wl.scale, True, window=wl.window,
+                                             sinks=x["sinks"][[h]] if wl.sinks else None)
+        compare(tuple(g[sl] for g in got), want[:3], f"{name} head {h}")
+        if wl.sinks:
+            compare_dsinks(ds[[h]], *(x[n][sl] for n in ("q", "k", "v", "dout")), wl.window, x["sinks"][[h]], [0],
+                           f"{name} head {h}")
+        return
     if not wl.varlen:
         got = run(x["q"], x["k"], x["v"], x["dout"], wl.causal)
         heads = [wl.H - 3]
