@@ -402,17 +402,25 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
       for (int c = 0; c < NDC; ++c) x = mfma32(frag_rows<D>(t_rows, 32 * qb, c, l32, hh), kvf[c], x);
       // query rows 32qb + 8(r/4) + 4hh + r%4 of this lane's key
       if (s_side) {
+        // the masks only where this wave's 32 keys and the half's 32 rows
+        // cross the diagonal or the window's lower edge
+        const int qr_off = q0 + 32 * qb + off;
+        const bool partial = (CAUSAL && kw0 + 31 > qr_off) || (LOCAL && W > 0 && kw0 <= qr_off + 31 - W);
+        if (partial) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i_off = qr_off + 8 * (r >> 2) + 4 * hh + (r & 3);  // query row + off
+            if (CAUSAL) x[r] = krow > i_off ? -INFINITY : x[r];
+            if (LOCAL && W > 0) x[r] = krow <= i_off - W ? -INFINITY : x[r];
+          }
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const f32x4 lv = *(const f32x4*)(tlse + 32 * qb + 8 * g + 4 * hh);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            float sv = x[r];
-            const int i_off = q0 + 32 * qb + 8 * g + 4 * hh + e + off;  // query row + off
-            if (CAUSAL) sv = krow > i_off ? -INFINITY : sv;
-            if (LOCAL && W > 0) sv = krow <= i_off - W ? -INFINITY : sv;
-            x[r] = fast_exp2(fmaf(sv, sl2, -lv[e]));
+            x[r] = fast_exp2(fmaf(x[r], sl2, -lv[e]));
           }
           *(f32x4*)(pbuf + 256 * g + 4 * lane) = f32x4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
         }
