@@ -621,7 +621,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
     const unsigned char* tv = tk + TILE;
     // skip the tiles no row of this wave sees (causal, window); a branch
     // around the whole step, so the accumulators stay where they are
-    if (k0 < w_end && k0 + BN > w_lo) {
+    // the tile step, with the masks (causal, window) compiled in or out
+    auto tile_step = [&](auto masked) {
       // Four MFMA phases written out as a software pipeline (sched_barrier
       // fences; left to itself the compiler read each operand one MFMA
       // ahead and ran the vector work between MFMA blocks):
@@ -654,8 +655,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
       auto vec_elem = [&](const int kbi, const int r) {
         float sv = st[kbi][r];
         const int kk = k0 + 32 * kbi + 8 * (r >> 2) + (r & 3);
-        if (CAUSAL) sv = kk >= lim_h ? -INFINITY : sv;
-        if (LOCAL) sv = kk < lo_h ? -INFINITY : sv;
+        if (decltype(masked)::value && CAUSAL) sv = kk >= lim_h ? -INFINITY : sv;
+        if (decltype(masked)::value && LOCAL) sv = kk < lo_h ? -INFINITY : sv;
         const float pv = fast_exp2(fmaf(sv, sl2, neg_lse));
         dpt[kbi][r] = pv * (dpt[kbi][r] - del);
         if (r == 7 || r == 15) sb[kbi][r >> 3] = half_bf16(dpt[kbi], r >> 3);
@@ -686,6 +687,17 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
         }
         __builtin_amdgcn_sched_barrier(0);
       });
+    };
+    if (k0 < w_end && k0 + BN > w_lo) {
+      // masks only on tiles that cross the diagonal or the window's lower
+      // edge for some row of this wave; the packed-sequence kernels keep one
+      // masked copy (two copies of the step spill there)
+      const bool partial = (CAUSAL && k0 + BN - 1 > qw0 + off) || (LOCAL && W > 0 && k0 < qw0 + 31 + off - W + 1);
+      if (VARLEN || partial) {
+        tile_step(std::true_type{});
+      } else {
+        tile_step(std::false_type{});
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
