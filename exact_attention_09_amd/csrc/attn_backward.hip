@@ -380,73 +380,149 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
   lstore(0);
   __syncthreads();
 
-  for (int s = 0; s < nsteps; ++s) {
-    const int stage = s & 1;
-    if (s + 1 < nsteps) gload(s + 1);
-    int h, q0;
-    step_src(s, h, q0);
-    (void)h;
-    const unsigned char* tq = smem + stage * STAGE;
-    const unsigned char* tdo = tq + TILE;
-    const float* tlse = (const float*)(tq + 2 * TILE);
-    const float* tdel = tlse + BQ;
-    // S side: rows of Q for S, columns of dO for dV; dP side: rows of dO
-    // for dP, columns of Q for dK
-    const unsigned char* t_rows = s_side ? tq : tdo;
-    const unsigned char* t_cols = s_side ? tdo : tq;
+  // One 64-row tile per step, as two 32-row halves.  Both sides first run
+  // the S (dP) products of both halves; the S side then forms P of half 0
+  // and, after the first barrier, runs dV of half 0 while forming P of half
+  // 1, so that its exponentials overlap MFMAs (its own and its partner's)
+  // instead of leaving the SIMD's matrix unit idle.  Each side has its own
+  // straight-line step (the compiler schedules within one block); both meet
+  // the same three barriers per step.
+  static_assert(NQB == 2, "a step is two 32-row halves");
+  // S (S side) or dP (dP side) of half qb: rows of t_rows against this
+  // lane's K or V row; query rows 32qb + 8(r/4) + 4hh + r%4 of this key
+  auto rows_product = [&](const unsigned char* t_rows, const int qb) {
+    f32x16 x = f32x16{};
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      float* pbuf = (float*)(smem + 2 * STAGE + (kb * NQB + qb) * PBUF);
-      f32x16 x = f32x16{};
+    for (int c = 0; c < NDC; ++c) x = mfma32(frag_rows<D>(t_rows, 32 * qb, c, l32, hh), kvf[c], x);
+    return x;
+  };
+  // dV^T += dO^T P (S side), dK^T += Q^T dS (dP side), 16 queries per product
+  auto cols_product = [&](const unsigned char* t_cols, const f32x16& x, const int qb) {
 #pragma unroll
-      for (int c = 0; c < NDC; ++c) x = mfma32(frag_rows<D>(t_rows, 32 * qb, c, l32, hh), kvf[c], x);
-      // query rows 32qb + 8(r/4) + 4hh + r%4 of this lane's key
-      if (s_side) {
-        // the masks only where this wave's 32 keys and the half's 32 rows
-        // cross the diagonal or the window's lower edge
-        const int qr_off = q0 + 32 * qb + off;
-        const bool partial = (CAUSAL && kw0 + 31 > qr_off) || (LOCAL && W > 0 && kw0 <= qr_off + 31 - W);
-        if (partial) {
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const bf16x8 xb = half_bf16(x, h2);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i_off = qr_off + 8 * (r >> 2) + 4 * hh + (r & 3);  // query row + off
-            if (CAUSAL) x[r] = krow > i_off ? -INFINITY : x[r];
-            if (LOCAL && W > 0) x[r] = krow <= i_off - W ? -INFINITY : x[r];
-          }
+      for (int db = 0; db < NDB; ++db)
+        acc[db] = mfma32(frag_cols<D>(t_cols, 2 * qb + h2, db, tr_row, tr_col), xb, acc[db]);
+    }
+  };
+  auto pbuf_of = [&](const int qb) { return (float*)(smem + 2 * STAGE + (kb * NQB + qb) * PBUF); };
+  if (s_side) {
+    // P = exp2(S scale' - LSE') of half qb, masked, to this pair's LDS buffer
+    // in fp32: the masks (only where this wave's 32 keys and the half's 32
+    // rows cross the diagonal or the window's lower edge) ...
+    auto mask_s = [&](f32x16& x, const int q0, const int qb) {
+      const int qr_off = q0 + 32 * qb + off;
+      const bool partial = (CAUSAL && kw0 + 31 > qr_off) || (LOCAL && W > 0 && kw0 <= qr_off + 31 - W);
+      if (partial) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i_off = qr_off + 8 * (r >> 2) + 4 * hh + (r & 3);  // query row + off
+          if (CAUSAL) x[r] = krow > i_off ? -INFINITY : x[r];
+          if (LOCAL && W > 0) x[r] = krow <= i_off - W ? -INFINITY : x[r];
         }
+      }
+    };
+    // ... then element r (the four of a group stored once the last is done)
+    auto p_elem = [&](f32x16& x, const f32x4* lv, float* pbuf, const int r) {
+      x[r] = fast_exp2(fmaf(x[r], sl2, -lv[r >> 2][r & 3]));
+      if ((r & 3) == 3) {
+        const int g = r >> 2;
+        *(f32x4*)(pbuf + 256 * g + 4 * lane) = f32x4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+      }
+    };
+    constexpr int AH = 2, R = AH + 1;
+    for (int s = 0; s < nsteps; ++s) {
+      const int stage = s & 1;
+      if (s + 1 < nsteps) gload(s + 1);
+      int h, q0;
+      step_src(s, h, q0);
+      (void)h;
+      const unsigned char* tq = smem + stage * STAGE;
+      const unsigned char* tdo = tq + TILE;
+      const float* tlse = (const float*)(tq + 2 * TILE);
+      f32x4 lv0[4], lv1[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 lv = *(const f32x4*)(tlse + 32 * qb + 8 * g + 4 * hh);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            x[r] = fast_exp2(fmaf(x[r], sl2, -lv[e]));
-          }
-          *(f32x4*)(pbuf + 256 * g + 4 * lane) = f32x4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
-        }
+      for (int g = 0; g < 4; ++g) {
+        lv0[g] = *(const f32x4*)(tlse + 8 * g + 4 * hh);
+        lv1[g] = *(const f32x4*)(tlse + 32 + 8 * g + 4 * hh);
+      }
+      f32x16 x0 = rows_product(tq, 0);
+      mask_s(x0, q0, 0);
+      // S of half 1, with P of half 0 spread over its MFMAs (operands read
+      // AH MFMAs ahead; sched_barrier keeps the order)
+      f32x16 x1 = f32x16{};
+      {
+        bf16x8 fr[R];
+        static_for<AH>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          fr[i] = frag_rows<D>(tq, 32, i, l32, hh);
+        });
+        constexpr int EPM = 16 / NDC;  // elements of P per MFMA
+        static_for<NDC>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          x1 = mfma32(fr[i % R], kvf[i], x1);
+          if constexpr (i + AH < NDC) fr[(i + AH) % R] = frag_rows<D>(tq, 32, i + AH, l32, hh);
+          static_for<EPM>([&](auto ec) { p_elem(x0, lv0, pbuf_of(0), EPM * i + decltype(ec)::value); });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+      mask_s(x1, q0, 1);
+      __syncthreads();
+      // dV of half 0, with P of half 1 spread over its MFMAs
+      {
+        constexpr int NM = 2 * NDB;    // MFMAs of the product
+        constexpr int EPM = 16 / NM;   // elements of P per MFMA
+        bf16x8 fc[R];
+        const bf16x8 xb[2] = {half_bf16(x0, 0), half_bf16(x0, 1)};
+        static_for<AH>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          fc[i] = frag_cols<D>(tdo, i / NDB, i % NDB, tr_row, tr_col);
+        });
+        static_for<NM>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          acc[i % NDB] = mfma32(fc[i % R], xb[i / NDB], acc[i % NDB]);
+          if constexpr (i + AH < NM) fc[(i + AH) % R] = frag_cols<D>(tdo, (i + AH) / NDB, (i + AH) % NDB, tr_row, tr_col);
+          static_for<EPM>([&](auto ec) { p_elem(x1, lv1, pbuf_of(1), EPM * i + decltype(ec)::value); });
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
       __syncthreads();
-      if (!s_side) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 pv = *(const f32x4*)(pbuf + 256 * g + 4 * lane);
-          const f32x4 dl = *(const f32x4*)(tdel + 32 * qb + 8 * g + 4 * hh);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * g + e] = pv[e] * (x[4 * g + e] - dl[e]);
-        }
-      }
-      // dV^T += dO^T P (S side), dK^T += Q^T dS (dP side), 16 queries per product
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 xb = half_bf16(x, h2);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          acc[db] = mfma32(frag_cols<D>(t_cols, 2 * qb + h2, db, tr_row, tr_col), xb, acc[db]);
-      }
+      cols_product(tdo, x1, 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      if (s + 1 < nsteps) lstore(stage ^ 1);
+      __syncthreads();
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    if (s + 1 < nsteps) lstore(stage ^ 1);
-    __syncthreads();
+  } else {
+    // dS = P (dP - Delta), P from the partner's buffer
+    auto make_ds = [&](f32x16& x, const float* tdel, const int qb) {
+      const float* pbuf = pbuf_of(qb);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 pv = *(const f32x4*)(pbuf + 256 * g + 4 * lane);
+        const f32x4 dl = *(const f32x4*)(tdel + 32 * qb + 8 * g + 4 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * g + e] = pv[e] * (x[4 * g + e] - dl[e]);
+      }
+    };
+    for (int s = 0; s < nsteps; ++s) {
+      const int stage = s & 1;
+      if (s + 1 < nsteps) gload(s + 1);
+      const unsigned char* tq = smem + stage * STAGE;
+      const unsigned char* tdo = tq + TILE;
+      const float* tdel = (const float*)(tq + 2 * TILE) + BQ;
+      f32x16 x0 = rows_product(tdo, 0);
+      f32x16 x1 = rows_product(tdo, 1);
+      __syncthreads();
+      make_ds(x0, tdel, 0);
+      cols_product(tq, x0, 0);
+      __syncthreads();
+      make_ds(x1, tdel, 1);
+      cols_product(tq, x1, 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      if (s + 1 < nsteps) lstore(stage ^ 1);
+      __syncthreads();
+    }
   }
 
   // dV = dV^T^T (S side), dK = s dK^T^T (dP side): this lane's key row
