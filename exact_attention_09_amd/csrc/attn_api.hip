@@ -138,7 +138,9 @@ attn_status forward(const void* q, const void* k, const void* v, void* o, float*
   const long double q_elems = (long double)(varlen ? 1 : B) * H * Sq * d;
   const long double kv_elems = (long double)(varlen ? 1 : B) * Hkv * Skv * d;
   if (q_elems > 9.0e18L || kv_elems > 9.0e18L) return fail(ATTN_EINVAL, "tensor too large");
-  if ((long)H * d > 0x3fffffffL) return fail(ATTN_EINVAL, "H * d too large");
+  // a K/V row (H * d elements apart in BSHD) times the rows of one tile (at
+  // most 128) must stay inside the 32-bit byte range of a buffer descriptor
+  if ((long)H * d >= (1L << 23)) return fail(ATTN_EINVAL, "H * d too large (must be below 2^23)");
 
   attn::Params p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.cu = cu_seqlens;

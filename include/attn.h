@@ -53,7 +53,10 @@
  * throughout (no low-precision step).
  *
  * Errors: arguments are validated on the host before any HIP call; on
- * failure nothing is launched and no output is touched.  HIP failures give
+ * failure nothing is launched and no output is touched.  Sizes: H * d must be
+ * below 2^23 (a K/V row of a BSHD tensor times the rows of one tile must fit
+ * the 32-bit byte range of a buffer descriptor), and every tensor below
+ * 9e18 elements.  HIP failures give
  * ATTN_EHIP.  attn_last_error() returns a per-thread message about the last
  * failure.  Execution is asynchronous on `stream`: ATTN_OK means enqueued.
  *

@@ -56,6 +56,7 @@ def call(lib, *, q=P, k=P, v=P, o=Q2, lse=None, B=1, H=4, Hkv=2, Sq=8, Skv=8, d=
     (dict(H=6, Hkv=4), ea.ATTN_EINVAL),
     (dict(Hkv=0), ea.ATTN_EINVAL),
     (dict(d=96), ea.ATTN_EUNSUPPORTED),
+    (dict(H=65536, Hkv=65536, d=128), ea.ATTN_EINVAL),  # H * d = 2^23
     (dict(d=256), ea.ATTN_EUNSUPPORTED),
     (dict(scale=0.0), ea.ATTN_EINVAL),
     (dict(scale=-0.5), ea.ATTN_EINVAL),
