@@ -3,8 +3,10 @@
 A step is one attn_fwd call over the headline workload (B=1, H=32,
 Sq=Skv=8192, d=128, bf16, non-causal), inputs resident in HBM.  The JSON line
 reports whole-job TFLOP/s (4*B*H*Sq*Skv*d flop per step), the prefill
-kernel's roofline (MFMA bf16 peak), the fp64 CPU oracle timed on a bounded
-sample of the same workload, and, under "workloads", the other shapes: the
+kernel's roofline (MFMA bf16 peak), the median and minimum step, the fp64
+CPU oracle timed on every row of the same workload (also the reference of
+the headline's parity record; sampled rows for the other forward workloads),
+and, under "workloads", the other shapes: the
 causal 8K run, the 2K d=64 causal run, varlen grouped-query prefill,
 sliding-window attention with sinks at 32K tokens, split-KV decode over a
 contiguous and a paged cache (HBM roofline), and the backward pass of the
@@ -70,26 +72,29 @@ def read_traffic(workload: str):
 
 
 def time_steps(fn, steps: int, warmup: int, stream):
-    """Warm up, then time `steps` calls: wall clock between two device
-    synchronisations, and HIP events on the launch stream around the same
-    region (launches back to back, so the event time per step is the kernel
-    time without host-side gaps between steps)."""
+    """Warm up, then time `steps` calls back to back: wall clock between two
+    device synchronisations, and HIP events on the launch stream at every step
+    boundary (mean over the region, plus the median and minimum step)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    a.record(stream)
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         fn()
-    b.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return {"wall_ms_per_step": 1e3 * wall / steps, "event_ms_mean": a.elapsed_time(b) / steps}
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    mid = steps // 2
+    median = per[mid] if steps % 2 else 0.5 * (per[mid - 1] + per[mid])
+    return {"wall_ms_per_step": 1e3 * wall / steps, "event_ms_mean": ev[0].elapsed_time(ev[steps]) / steps,
+            "event_ms_median": median, "event_ms_min": per[0]}
 
 
-def run_workload(name: str, steps: int, warmup: int, inputs=None):
+def run_workload(name: str, steps: int, warmup: int, inputs=None, keep_outputs: bool = False):
     import numpy as np
     import torch
 
@@ -149,38 +154,99 @@ def run_workload(name: str, steps: int, warmup: int, inputs=None):
                            workspace=ws, stream=stream.cuda_stream)
 
     t = time_steps(step, steps, warmup, stream)
+    if keep_outputs and not wl.backward:
+        # the last step's outputs, for the parity record
+        t["outputs"] = (o.float().cpu().numpy(), lse.cpu().numpy())
     del q, k, v, o, lse, ws
     torch.cuda.empty_cache()
     return wl, ns, t
 
 
-def cpu_baseline(name: str, inputs, target_s: float = 15.0):
-    """The oracle as it stands, on a bounded sample of query rows of the
-    same workload (every key of each sampled row), on the host cores."""
+def cpu_threads() -> int:
+    """Host threads for the oracle: the cores, at most 16 (a GPU machine allots 16
+    CPUs to each GPU)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def parity_record(o, lse, o_ref, lse_ref, rows_compared: int) -> dict:
+    """max |dO| (raw and against the bf16-rounded oracle), elements above
+    1e-2, max |dLSE|, with positions (indices into the compared rows)."""
+    import numpy as np
+    o = np.asarray(o, np.float64)
+    o_ref = np.asarray(o_ref, np.float64).reshape(o.shape)
+    lse = np.asarray(lse, np.float64).reshape(-1)
+    lse_ref = np.asarray(lse_ref, np.float64).reshape(-1)
+    err = np.abs(o - o_ref)
+    i = np.unravel_index(int(np.argmax(err)), err.shape)
+    f = np.ascontiguousarray(o_ref.astype(np.float32)).view(np.uint32).astype(np.uint64)
+    rb = (((f + 0x7FFF + ((f >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    fin = np.isfinite(lse_ref)
+    same_inf = bool(np.array_equal(np.isneginf(lse), np.isneginf(lse_ref)))
+    lerr = np.abs(lse[fin] - lse_ref[fin]) if fin.any() else np.zeros(1)
+    j = int(np.argmax(lerr))
+    return {"rows": int(rows_compared), "max_dO": float(err[i]), "argmax": [int(x) for x in i],
+            "max_dO_vs_bf16_ref": float(np.abs(o - rb).max()), "n_over_1e-2": int((err > 1e-2).sum()),
+            "max_dLSE": float(lerr[j]), "argmax_lse": int(np.flatnonzero(fin)[j]) if fin.any() else -1,
+            "empty_rows_match": same_inf}
+
+
+def cpu_baseline(name: str, inputs, gpu_out, threads: int):
+    """The oracle as it stands on every query row of the headline workload
+    (every key of each row), on the host cores, timed; its output is also the
+    reference for the headline's parity record."""
     import numpy as np
 
     import oracle
     from exact_attention_09_amd.workloads import WORKLOADS, host_f32
     wl = WORKLOADS[name]
     q, k, v = (host_f32(inputs[t], wl.dtype) for t in ("q", "k", "v"))
-    threads = max(1, min(16, os.cpu_count() or 1))
-
-    def rows_for(n):
-        idx = np.arange(n, dtype=np.int64) * 7919 % (wl.B * wl.H * wl.Sq)
-        return np.stack([idx // (wl.H * wl.Sq), (idx // wl.Sq) % wl.H, idx % wl.Sq], axis=1)
-
-    n_cal = 4096
     t0 = time.perf_counter()
-    oracle.attention(q, k, v, wl.scale, wl.causal, rows=rows_for(n_cal), nthreads=threads)
-    cal = time.perf_counter() - t0
-    n = int(min(wl.B * wl.H * wl.Sq, max(n_cal, n_cal * target_s / max(cal, 1e-3))))
-    rows = rows_for(n)
-    t0 = time.perf_counter()
-    oracle.attention(q, k, v, wl.scale, wl.causal, rows=rows, nthreads=threads)
+    o_ref, lse_ref = oracle.attention(q, k, v, wl.scale, wl.causal, nthreads=threads)
     dt = time.perf_counter() - t0
-    flops = 4.0 * n * wl.Skv * wl.d
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} query rows of {name} (all {wl.Skv} keys each, fp64 naive), {dt:.1f} s"}
+    n = wl.B * wl.H * wl.Sq
+    flops = wl.flops()
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(),
+            "sample": f"all {n} query rows of {name} (all {wl.Skv} keys each, fp64 naive), {dt:.1f} s",
+            "threads_note": "at most 16 threads: a GPU box allots 16 CPUs to each GPU"}
+    parity = parity_record(gpu_out[0], gpu_out[1], o_ref, lse_ref, n) if gpu_out is not None else None
+    return base, parity
+
+
+def sampled_parity(name: str, gpu_out, threads: int, n_rows: int = 2048):
+    """Parity of another forward workload's last GPU step on seeded sample
+    rows (every row when there are few), for the record."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_09_amd.workloads import WORKLOADS, host_f32
+    wl = WORKLOADS[name]
+    x = wl.make_inputs()
+    q, k, v = (host_f32(x[t], wl.dtype) for t in ("q", "k", "v"))
+    o, lse = gpu_out
+    kw = {}
+    if wl.window > 0 or wl.sinks:
+        kw = {"window": wl.window, "sinks": x["sinks"]}
+    rng = np.random.default_rng(1000 + wl.wid)
+    if wl.varlen:
+        cu = x["cu_seqlens"]
+        q, k, v = q[0], k[0], v[0]
+        total = wl.H * wl.total_tokens
+        flat = np.arange(total) if total <= n_rows else rng.choice(total, n_rows, replace=False)
+        hh, tt = flat // wl.total_tokens, flat % wl.total_tokens
+        bb = np.searchsorted(cu, tt, side="right") - 1
+        rows = np.stack([bb, hh, tt - cu[bb]], axis=1).astype(np.int64)
+        o_ref, lse_ref = oracle.attention(q, k, v, wl.scale, wl.causal, cu_seqlens=cu, rows=rows, nthreads=threads,
+                                          **kw)
+        og, lg = o[0, hh, tt], lse[0, hh, tt]
+    else:
+        total = wl.B * wl.H * wl.Sq
+        flat = np.arange(total) if total <= n_rows else rng.choice(total, n_rows, replace=False)
+        b, h, i = flat // (wl.H * wl.Sq), (flat // wl.Sq) % wl.H, flat % wl.Sq
+        rows = np.stack([b, h, i], axis=1).astype(np.int64)
+        o_ref, lse_ref = oracle.attention(q, k, v, wl.scale, wl.causal, rows=rows, nthreads=threads, **kw)
+        og, lg = o[b, h, i], lse[b, h, i]
+    return parity_record(og, lg, o_ref, lse_ref, len(rows))
 
 
 def main(argv=None):
@@ -226,7 +292,7 @@ def main(argv=None):
     wl = WORKLOADS[HEADLINE]
     inputs = wl.make_inputs()
     print(f"# timing {HEADLINE}", file=sys.stderr, flush=True)
-    _, _, t = run_workload(HEADLINE, args.steps, args.warmup, inputs)
+    _, _, t = run_workload(HEADLINE, args.steps, args.warmup, inputs, keep_outputs=not args.quick)
     flops = wl.flops()
     value = flops / (t["wall_ms_per_step"] * 1e-3) / 1e12
     achieved = flops / (t["event_ms_mean"] * 1e-3) / 1e12
@@ -238,20 +304,27 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": HEADLINE, "B": wl.B, "H": wl.H, "Hkv": wl.Hkv, "Sq": wl.Sq, "Skv": wl.Skv,
                    "d": wl.d, "causal": wl.causal, "layout": "BHSD", "inputs": "N(0,1) seeded"},
+        "median_ms": round(t["event_ms_median"], 4), "min_ms": round(t["event_ms_min"], 4),
+        "mean_ms": round(t["event_ms_mean"], 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "prefill_pp_kernel<128,false,false,false,false>",
-                     "launch_ms_mean": round(t["event_ms_mean"], 4)},
+                     "launch_ms_mean": round(t["event_ms_mean"], 4),
+                     "frac_at_median": round(flops / (t["event_ms_median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
     }
     workloads = {}
+    outputs = {}
     if not args.quick:
         for name in ("mha_causal_s8192_d128", "mha_causal_s2048_d64", "varlen_gqa_causal_d128",
                      "swa_sink_s32768_d128", "decode_gqa_s16384_d128", "decode_paged_gqa_s16384_d128",
                      "bwd_mha_s8192_d128", "bwd_mha_causal_s8192_d128", "bwd_varlen_gqa_causal_d128",
                      "bwd_swa_sink_s8192_d128"):
             print(f"# timing {name}", file=sys.stderr, flush=True)
-            w, ns, tt = run_workload(name, args.steps, args.warmup)
-            entry = {"ms_per_step": round(tt["wall_ms_per_step"], 4), "launch_ms_mean": round(tt["event_ms_mean"], 4)}
+            w, ns, tt = run_workload(name, args.steps, args.warmup, keep_outputs=not WORKLOADS[name].paged)
+            if "outputs" in tt:
+                outputs[name] = tt.pop("outputs")
+            entry = {"ms_per_step": round(tt["wall_ms_per_step"], 4), "launch_ms_mean": round(tt["event_ms_mean"], 4),
+                     "median_ms": round(tt["event_ms_median"], 4), "min_ms": round(tt["event_ms_min"], 4)}
             if w.Sq == 1 and not w.varlen:
                 gbps = w.bytes(ns) / (tt["event_ms_mean"] * 1e-3) / 1e9
                 entry.update({"GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
@@ -261,8 +334,17 @@ def main(argv=None):
                 entry.update({"TFLOP/s": round(tf, 2), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4),
                               "flops_per_step": w.flops()})
             workloads[name] = entry
+        # the CPU leg: the oracle on every headline row (timed), which is also
+        # the headline's parity reference, then sampled parity of the other
+        # forward workloads' last steps
         print("# cpu baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(HEADLINE, inputs)
+        threads = cpu_threads()
+        base, parity = cpu_baseline(HEADLINE, inputs, t.get("outputs"), threads)
+        line["cpu_baseline"] = base
+        line["parity"] = {HEADLINE: parity}
+        for name, out in outputs.items():
+            print(f"# parity {name}", file=sys.stderr, flush=True)
+            line["parity"][name] = sampled_parity(name, out, threads)
     else:
         line["cpu_baseline"] = None
     line["workloads"] = workloads

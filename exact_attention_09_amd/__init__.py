@@ -42,9 +42,13 @@ EXPORTED = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_window_sink", "
             "attn_decode_num_splits", "attn_status_string", "attn_last_error")
 
 
+ATTN_FLAG_BASIC_PREFILL = 1
+ATTN_FLAG_NO_PERSIST = 2
+
+
 class AttnOpts(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint)]
 
 
 class AttnError(RuntimeError):
@@ -149,13 +153,14 @@ def _shapes(q, k, cu_seqlens):
 
 def attn_fwd_ex(q, k, v, o=None, lse=None, *, causal: bool = False, scale: float | None = None,
                 cu_seqlens=None, stream=None, dtype: int | None = None, num_splits: int = 0,
-                workspace=None, want_lse: bool = True):
+                workspace=None, want_lse: bool = True, flags: int = 0):
     """Run the forward pass through ``attn_fwd_ex``.
 
     q [B,H,Sq,d], k/v [B,Hkv,Skv,d] (varlen: [1,H,T,d], [1,Hkv,T,d] with an
     int32 ``cu_seqlens`` of B+1 prefix sums on the GPU).  ``o``/``lse`` are
     allocated when not given (``lse`` only if ``want_lse``).  ``scale``
     defaults to 1/sqrt(d).  ``stream`` defaults to torch's current stream.
+    ``flags`` are the ``ATTN_FLAG_*`` kernel selection bits.
     Returns ``(o, lse)``.
     """
     import torch
@@ -182,7 +187,7 @@ def attn_fwd_ex(q, k, v, o=None, lse=None, *, causal: bool = False, scale: float
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     opts = AttnOpts(int(num_splits), workspace.data_ptr() if workspace is not None else None,
-                    workspace.numel() * workspace.element_size() if workspace is not None else 0)
+                    workspace.numel() * workspace.element_size() if workspace is not None else 0, int(flags))
     st = lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Sq, Skv, d,
                          float(scale), int(bool(causal)), _ptr(cu_seqlens), ctypes.c_void_p(stream),
                          int(dtype), ctypes.byref(opts))

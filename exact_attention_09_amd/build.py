@@ -1,7 +1,9 @@
 """Build the gfx950 attention library (``libattn09.so``) with hipcc.
 
 Every ``csrc/*.hip`` file is compiled for gfx950 in parallel and linked into
-one shared library next to this file.  Packed fp32 instructions are turned
+one shared library next to this file; ``csrc/attn_sched_host.cpp`` (host code
+over the work-decomposition functions, for the unit tests) goes into a small
+library of its own.  Packed fp32 instructions are turned
 off (``-packed-fp32-ops``); hipcc's host pass warns that it does not know the
 feature, which is harmless.
 """
@@ -21,6 +23,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn09.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+# host-only library over the work-decomposition functions, for the unit tests
+SCHED_LIB_PATH = os.path.join(HERE, "libattn09_sched.so")
 ARCH = "gfx950"
 
 
@@ -66,7 +70,21 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{_quiet(r.stdout + r.stderr)}")
     os.replace(tmp, LIB_PATH)
+    build_sched(cc)
     return LIB_PATH
+
+
+def build_sched(cc=None) -> str:
+    """Compile attn_sched_host.cpp (host code only) into libattn09_sched.so."""
+    cc = cc or hipcc()
+    tmp = SCHED_LIB_PATH + ".tmp"
+    cmd = [cc, "-x", "hip", "--cuda-host-only", f"--offload-arch={ARCH}", "-O2", "-std=c++17", "-fPIC", "-shared",
+           "-Wall", "-I", CSRC, os.path.join(CSRC, "attn_sched_host.cpp"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for attn_sched_host.cpp:\n{_quiet(r.stdout + r.stderr)}")
+    os.replace(tmp, SCHED_LIB_PATH)
+    return SCHED_LIB_PATH
 
 
 if __name__ == "__main__":

@@ -5,7 +5,6 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 
 #include "attn.h"
@@ -35,13 +34,6 @@ constexpr size_t kWsAlign = 256;
 size_t ws_lse_offset(long rows, int d, int splits) {
   const size_t o_bytes = (size_t)rows * splits * d * sizeof(float);
   return (o_bytes + kWsAlign - 1) / kWsAlign * kWsAlign;
-}
-
-int env_splits() {
-  const char* e = getenv("ATTN_NUM_SPLITS");
-  if (e == nullptr || *e == '\0') return 0;
-  const int v = atoi(e);
-  return (v >= 1 && v <= ATTN_MAX_SPLITS) ? v : 0;
 }
 
 // Enough workgroups to cover the 256 CUs a few times over, chunks of at
@@ -93,10 +85,7 @@ size_t attn_workspace_bytes(int B, int H, int d, int num_splits) {
   return ws_lse_offset(rows, d, num_splits) + (size_t)rows * num_splits * sizeof(float);
 }
 
-int attn_decode_num_splits(int B, int Hkv, int Skv) {
-  const int e = env_splits();
-  return e > 0 ? e : heuristic_splits(B, Hkv, Skv);
-}
+int attn_decode_num_splits(int B, int Hkv, int Skv) { return heuristic_splits(B, Hkv, Skv); }
 
 }  // extern "C"
 
@@ -118,6 +107,9 @@ attn_status forward(const void* q, const void* k, const void* v, void* o, float*
     return fail(ATTN_EINVAL, "negative size (B=%d H=%d Hkv=%d Sq=%d Skv=%d d=%d)", B, H, Hkv, Sq, Skv, d);
   if (opts != nullptr && (opts->num_splits < 0 || opts->num_splits > ATTN_MAX_SPLITS))
     return fail(ATTN_EINVAL, "num_splits %d outside [0, %d]", opts->num_splits, ATTN_MAX_SPLITS);
+  const unsigned flags = opts != nullptr ? opts->flags : 0u;
+  if ((flags & ~(ATTN_FLAG_BASIC_PREFILL | ATTN_FLAG_NO_PERSIST)) != 0)
+    return fail(ATTN_EINVAL, "unknown flag bits 0x%x", flags);
   if (B == 0 || H == 0 || Sq == 0) return ATTN_OK;  // nothing to compute
   if (q == nullptr || o == nullptr) return fail(ATTN_EINVAL, "q and o must not be NULL");
   if (Skv > 0 && (k == nullptr || v == nullptr))
@@ -165,9 +157,9 @@ attn_status forward(const void* q, const void* k, const void* v, void* o, float*
 
   const bool decode = !varlen && Sq == 1;
   if (!decode) {
-    // ATTN_BASIC_PREFILL selects the basic tiled kernel instead (it has no
-    // window or sink)
-    const bool pingpong = bf16 && (local || p.bshd || getenv("ATTN_BASIC_PREFILL") == nullptr);
+    // ATTN_FLAG_BASIC_PREFILL selects the basic tiled kernel instead (it has
+    // no window, sink or BSHD layout)
+    const bool pingpong = bf16 && (local || p.bshd || (flags & ATTN_FLAG_BASIC_PREFILL) == 0);
     const int bm = !bf16 ? attn::f32_block_m()
                          : (pingpong ? attn::prefill_pp_block_m() : attn::prefill_bf16_block_m());
     const long tiles = varlen ? (long)Sq / bm + B : attn::ceil_div(Sq, bm);
@@ -179,9 +171,9 @@ attn_status forward(const void* q, const void* k, const void* v, void* o, float*
     // light causal tiles): dense when the items divide evenly over the CUs,
     // varlen when locating an item (a scan over sequences and tile indices)
     // stays short; otherwise one workgroup per item and the hardware
-    // dispatcher balances.  ATTN_NO_PERSIST forces the latter.
+    // dispatcher balances.  ATTN_FLAG_NO_PERSIST forces the latter.
     p.persist_c = 0;
-    if (pingpong && getenv("ATTN_NO_PERSIST") == nullptr) {
+    if (pingpong && (flags & ATTN_FLAG_NO_PERSIST) == 0) {
       const int cus = device_cus();
       const long c = cus / 8;
       const bool fits = varlen ? H % 8 == 0 && B <= 1024 && (long)B * attn::ceil_div(Sq, bm) <= 1L << 16
@@ -283,6 +275,8 @@ attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cac
                 max_pages, num_pages);
   if (opts != nullptr && (opts->num_splits < 0 || opts->num_splits > ATTN_MAX_SPLITS))
     return fail(ATTN_EINVAL, "num_splits %d outside [0, %d]", opts->num_splits, ATTN_MAX_SPLITS);
+  if (opts != nullptr && (opts->flags & ~(ATTN_FLAG_BASIC_PREFILL | ATTN_FLAG_NO_PERSIST)) != 0)
+    return fail(ATTN_EINVAL, "unknown flag bits 0x%x", opts->flags);
   if (B == 0 || H == 0) return ATTN_OK;  // nothing to compute
   if (q == nullptr || o == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
       seqlens_k == nullptr)
@@ -423,8 +417,9 @@ attn_status backward(const void* q, const void* k, const void* v, const void* o,
 
   if (Sq == 0) {  // dense only: a varlen call with no token returned above
     // no query: dK = dV = 0
+    // rows counted as B * Hkv * Skv in 64 bits by the fill kernel's launcher
     attn::Params z = p;
-    z.B = 1; z.H = 1; z.Sq = (int)((long)B * Hkv * Skv); z.cu = nullptr; z.lse = nullptr; z.sinks = nullptr;
+    z.B = B; z.H = Hkv; z.Sq = Skv; z.cu = nullptr; z.lse = nullptr; z.sinks = nullptr;
     z.o = dk;
     hipError_t e = attn::launch_fill_empty(z, true, st);
     if (e == hipSuccess) {
@@ -432,6 +427,8 @@ attn_status backward(const void* q, const void* k, const void* v, const void* o,
       e = attn::launch_fill_empty(z, true, st);
     }
     if (e == hipSuccess && sinks != nullptr) {  // dsinks = 0: H fp32 zeros through the same fill kernel
+      z.B = 1;
+      z.H = 1;
       z.Sq = 1;
       z.d = H;
       z.o = dsinks;

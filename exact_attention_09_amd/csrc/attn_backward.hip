@@ -141,88 +141,6 @@ __device__ inline bf16x8 half_bf16(const f32x16& a, int h) {
   return to_bf16x8(a[rb + 0], a[rb + 1], a[rb + 2], a[rb + 3], a[rb + 4], a[rb + 5], a[rb + 6], a[rb + 7]);
 }
 
-// Varlen: the per-head tile index vt of packed sequences with `tile`-row
-// tiles (tiles of one sequence consecutive, sequences in order); sets the
-// sequence's first row s0, its length and the tile within it.  False past
-// the last tile.  Sequence bounds are clamped into [0, T].
-__device__ inline bool varlen_tile(const Params& p, int vt, int tile, int& s0, int& len, int& t_in) {
-  const int T = p.Sq;
-  int acc = 0;
-  for (int bb = 0; bb < p.B; ++bb) {
-    int a = p.cu[bb], e = p.cu[bb + 1];
-    a = a < 0 ? 0 : (a > T ? T : a);
-    e = e < a ? a : (e > T ? T : e);
-    const int nt = ceil_div(e - a, tile);
-    if (vt < acc + nt) {
-      s0 = a;
-      len = e - a;
-      t_in = vt - acc;
-      return true;
-    }
-    acc += nt;
-  }
-  return false;
-}
-
-// Varlen, causal: the items listed by work, heaviest first.  An item of
-// level r costs about r tile-pairs: key tile k of a sequence of n tiles has
-// level n - k (it sees the query tiles k .. n-1), query tile t level t + 1.
-// Levels run from the largest n down to 1; within a level, sequences in
-// order.  F(r) = sum_i max(0, n_i - r + 1) items have level >= r, so item f
-// has the level r with F(r+1) <= f < F(r) (binary search), and is the
-// (f - F(r+1))-th sequence with n_i >= r.  Sets s0, len and the level; false
-// past the last item.  Costs a few scans of cu_seqlens per workgroup, so it
-// is used for short sequence lists only.
-constexpr int kRankedSeqs = 64;
-__device__ inline bool varlen_ranked(const Params& p, int f, int tile, int& s0, int& len, int& level) {
-  const int T = p.Sq;
-  auto bounds = [&](int bb, int& a, int& e) {
-    a = p.cu[bb];
-    e = p.cu[bb + 1];
-    a = a < 0 ? 0 : (a > T ? T : a);
-    e = e < a ? a : (e > T ? T : e);
-  };
-  auto items_from = [&](int r) {  // F(r)
-    int acc = 0;
-    for (int bb = 0; bb < p.B; ++bb) {
-      int a, e;
-      bounds(bb, a, e);
-      const int n = ceil_div(e - a, tile) - r + 1;
-      acc += n > 0 ? n : 0;
-    }
-    return acc;
-  };
-  int nmax = 0;
-  for (int bb = 0; bb < p.B; ++bb) {
-    int a, e;
-    bounds(bb, a, e);
-    const int n = ceil_div(e - a, tile);
-    nmax = n > nmax ? n : nmax;
-  }
-  if (nmax == 0 || f >= items_from(1)) return false;
-  int lo = 1, hi = nmax;  // the largest r with F(r) > f
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (items_from(mid) > f) {
-      lo = mid;
-    } else {
-      hi = mid - 1;
-    }
-  }
-  level = lo;
-  int j = f - items_from(lo + 1);
-  for (int bb = 0; bb < p.B; ++bb) {
-    int a, e;
-    bounds(bb, a, e);
-    if (ceil_div(e - a, tile) >= level && j-- == 0) {
-      s0 = a;
-      len = e - a;
-      return true;
-    }
-  }
-  return false;
-}
-
 // ---------------------------------------------------------------- dK, dV
 
 // Keys stationary, two waves per 32 keys: workgroup (b, KV head, 128 keys)
@@ -278,11 +196,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
       // heaviest first over all KV heads: the heads interleaved
       kvh = (int)blockIdx.x % p.Hkv;
       int level;
-      if (!varlen_ranked(p, (int)blockIdx.x / p.Hkv, BK, s0, len, level)) return;
+      if (!varlen_ranked(p.cu, p.B, p.Sq, (int)blockIdx.x / p.Hkv, BK, s0, len, level)) return;
       kt = ceil_div(len, BK) - level;
     } else {
       kvh = (int)blockIdx.x / ktu;
-      if (!varlen_tile(p, (int)blockIdx.x - kvh * ktu, BK, s0, len, kt)) return;
+      if (!varlen_tile(p.cu, p.B, p.Sq, (int)blockIdx.x - kvh * ktu, BK, s0, len, kt)) return;
     }
     b = 0;
     sq = skv = len;
@@ -294,8 +212,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
     const int nbk = p.B * p.Hkv;
     const int item = CAUSAL ? (int)blockIdx.x : xcd_remap((int)blockIdx.x, nbk * ktiles);
     if (item < 0) return;
-    kt = CAUSAL ? item / nbk : item % ktiles;
-    const int bk = CAUSAL ? item - kt * nbk : item / ktiles;  // b * Hkv + kvh
+    int bk;  // b * Hkv + kvh
+    bwd_dkdv_item(item, nbk, ktiles, CAUSAL, kt, bk);
     b = bk / p.Hkv;
     kvh = bk - b * p.Hkv;
     sq = p.Sq;
@@ -583,11 +501,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
       // heaviest first over all query heads: the heads interleaved
       h = (int)blockIdx.x % p.H;
       int level;
-      if (!varlen_ranked(p, (int)blockIdx.x / p.H, BMQ, s0, len, level)) return;
+      if (!varlen_ranked(p.cu, p.B, p.Sq, (int)blockIdx.x / p.H, BMQ, s0, len, level)) return;
       tile = level - 1;
     } else {
       h = (int)blockIdx.x / qtu;
-      if (!varlen_tile(p, (int)blockIdx.x - h * qtu, BMQ, s0, len, tile)) return;
+      if (!varlen_tile(p.cu, p.B, p.Sq, (int)blockIdx.x - h * qtu, BMQ, s0, len, tile)) return;
     }
     sq = skv = len;
     row0 = (int64_t)h * p.Sq + s0;
@@ -597,8 +515,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
     const int nbh = p.B * p.H;
     const int item = CAUSAL ? (int)blockIdx.x : xcd_remap((int)blockIdx.x, nbh * qtiles);
     if (item < 0) return;
-    const int bh = CAUSAL ? item % nbh : item / qtiles;
-    tile = CAUSAL ? qtiles - 1 - item / nbh : item - bh * qtiles;
+    int bh;
+    bwd_dq_item(item, nbh, qtiles, CAUSAL, bh, tile);
     const int b = bh / p.H;
     const int h = bh - b * p.H;
     sq = p.Sq;

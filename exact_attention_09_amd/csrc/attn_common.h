@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 
 #include <utility>
+
+#include "attn_sched.h"
 #include <stdint.h>
 
 namespace attn {
@@ -49,23 +51,12 @@ struct Params {
 
 // ---------------------------------------------------------------- helpers
 
-__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
-
 // Keys a causal query block [q_lo, q_hi) may see (bottom-right alignment:
 // key j visible to row i iff j <= i + off).
 __host__ __device__ inline int causal_kv_end(int q_hi, int off, int skv) {
   long e = (long)q_hi + off;
   if (e < 0) e = 0;
   return e < skv ? (int)e : skv;
-}
-
-// Workgroups are handed to the 8 XCDs round robin; map the launch index so
-// that each XCD receives one contiguous range of work items (the query tiles
-// of a head share K/V through that XCD's L2).  Returns -1 for padding.
-__device__ inline int xcd_remap(int wg, int work_items) {
-  const int per = ceil_div(work_items, 8);
-  const int v = (wg % 8) * per + wg / 8;
-  return v < work_items ? v : -1;
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -50,31 +50,15 @@ __global__ __launch_bounds__(64) void f32_kernel(const Params p) {
     q_row0 = (int64_t)bh * sq;
     kv_row0 = ((int64_t)b * p.Hkv + h / p.group) * skv;
   } else {
-    const int v = blockIdx.x;
-    h = v / p.tiles_per_head;
-    const int vt = v - h * p.tiles_per_head;
-    const int T = p.Sq;
-    int acc = 0, start = 0;
-    tile = -1;
-    sq = 0;
-    for (int bb = 0; bb < p.B; ++bb) {
-      int s0 = p.cu[bb], s1 = p.cu[bb + 1];
-      s0 = s0 < 0 ? 0 : (s0 > T ? T : s0);
-      s1 = s1 < s0 ? s0 : (s1 > T ? T : s1);
-      const int nt = ceil_div(s1 - s0, BM);
-      if (vt < acc + nt) {
-        tile = vt - acc;
-        sq = s1 - s0;
-        start = s0;
-        break;
-      }
-      acc += nt;
-    }
-    if (tile < 0) return;
+    int bb;
+    if (!varlen_item(p.cu, p.B, p.Sq, BM, p.tiles_per_head, false, blockIdx.x, h, bb, tile)) return;
+    int s0, s1;
+    seq_bounds(p.cu, p.Sq, bb, s0, s1);
+    sq = s1 - s0;
     skv = sq;
     off = 0;
-    q_row0 = (int64_t)h * T + start;
-    kv_row0 = (int64_t)(h / p.group) * T + start;
+    q_row0 = (int64_t)h * p.Sq + s0;
+    kv_row0 = (int64_t)(h / p.group) * p.Sq + s0;
   }
 
   const float* __restrict__ Q = (const float*)p.q + q_row0 * D;

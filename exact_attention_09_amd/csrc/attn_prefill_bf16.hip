@@ -67,42 +67,23 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const Params p) {
   int h, tile, sq, skv, off;
   int64_t q_row0, kv_row0;
   if constexpr (!VARLEN) {
-    const int bh = v / p.tiles_per_head;
-    const int rank = v - bh * p.tiles_per_head;
-    tile = CAUSAL ? p.tiles_per_head - 1 - rank : rank;  // heavy tiles first
-    const int b = bh / p.H;
-    h = bh - b * p.H;
+    int b;
+    dense_item(v, p.tiles_per_head, p.H, CAUSAL, b, h, tile);  // heavy tiles first
     sq = p.Sq;
     skv = p.Skv;
     off = skv - sq;
-    q_row0 = (int64_t)bh * sq;
+    q_row0 = ((int64_t)b * p.H + h) * sq;
     kv_row0 = ((int64_t)b * p.Hkv + h / p.group) * skv;
   } else {
-    h = v / p.tiles_per_head;
-    int vt = v - h * p.tiles_per_head;
-    if (CAUSAL) vt = p.tiles_per_head - 1 - vt;
-    const int T = p.Sq;
-    int acc = 0, start = 0;
-    tile = -1;
-    sq = 0;
-    for (int bb = 0; bb < p.B; ++bb) {
-      int s0 = p.cu[bb], s1 = p.cu[bb + 1];
-      s0 = s0 < 0 ? 0 : (s0 > T ? T : s0);
-      s1 = s1 < s0 ? s0 : (s1 > T ? T : s1);
-      const int nt = ceil_div(s1 - s0, BM);
-      if (vt < acc + nt) {
-        tile = vt - acc;
-        sq = s1 - s0;
-        start = s0;
-        break;
-      }
-      acc += nt;
-    }
-    if (tile < 0) return;
+    int bb;
+    if (!varlen_item(p.cu, p.B, p.Sq, BM, p.tiles_per_head, CAUSAL, v, h, bb, tile)) return;
+    int s0, s1;
+    seq_bounds(p.cu, p.Sq, bb, s0, s1);
+    sq = s1 - s0;
     skv = sq;
     off = 0;
-    q_row0 = (int64_t)h * T + start;
-    kv_row0 = (int64_t)(h / p.group) * T + start;
+    q_row0 = (int64_t)h * p.Sq + s0;
+    kv_row0 = (int64_t)(h / p.group) * p.Sq + s0;
   }
 
   const __bf16* __restrict__ Q = (const __bf16*)p.q + q_row0 * D;

@@ -176,6 +176,19 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   const int nw = ceil_div(w_end, BN);
   // relative tile u is computed by this wave
   auto computes = [&](const int u) { return u >= 0 && t_first + u >= w_first && t_first + u < nw; };
+  // Rows that see at most 64 keys in all (the first rows of a causal
+  // sequence, short key sets) put their whole weight on a few P~ values, and
+  // rounding those to bf16 for the P~V product can move O by a few
+  // thousandths; with the output's own bf16 rounding that can pass 1e-2.
+  // For the first key tile, which holds all of such rows' keys, the vector
+  // phase runs the P~V product itself, split: P~ = hi + lo with hi =
+  // bf16(P~) (the usual operand) and lo = bf16(P~ - hi), two MFMAs per step,
+  // so the numerator carries P~ to about 2^-16; the next matrix phase then
+  // skips that tile's product.  Only the first key tile of a sequence's
+  // first query tile takes this path (the window variant keeps the plain
+  // product).
+  const bool few_keys = !LOCAL && (CAUSAL ? (qw0 + off + 1 <= 64) : (skv <= 64));
+  auto precise = [&](const int u) { return few_keys && t_first + u == 0; };
   // keys < lim (and >= lo under a window) are visible to this lane's row;
   // kept as lim - 4hh and lo - 4hh so that the per-register key offset they
   // are compared with stays wave-uniform
@@ -263,7 +276,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
         // matrix phase: P~V of tile t-1, then S^T of tile t.  Operand
         // fragments are double buffered in registers: the LDS reads of step
         // i+1 are in flight while the MFMAs of step i run.
-        const bool do_pv = computes(t - 1);
+        const bool do_pv = computes(t - 1) && !precise(t - 1);
         const bool do_qk = computes(t);
         // the matrix phase issues first on this SIMD; the other group's
         // vector work fills the issue slots the MFMAs leave free
@@ -420,6 +433,28 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
           ps = expo();
         }
         l_part += ps;
+        if (precise(t)) {
+          // the split P~V product of this tile (V of tile t is in stage
+          // t % STAGES); the fp32 P~ is recomputed with expo()'s
+          // instructions, so its bf16 part is pb exactly
+          const unsigned char* vb = smem + (t % STAGES) * STAGE_B + v_lane;
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) {
+            const f32x16& sk = s[kc >> 1];
+            const int rb = 8 * (kc & 1);
+            float lo[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) lo[j] = fast_exp2(fmaf(sk[rb + j], sl2, neg_ms)) - (float)pb[kc][j];
+            const bf16x8 pl = to_bf16x8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              const unsigned char* a = vb + (NDB * kc + db) * 1024;
+              const bf16x8 vf = join_tr(lds_read_tr16(a), lds_read_tr16(a + 512));
+              oacc[db] = mfma32(vf, pb[kc], oacc[db]);
+              oacc[db] = mfma32(vf, pl, oacc[db]);
+            }
+          }
+        }
       }
     }
     if (slot & 1) {
@@ -482,16 +517,14 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   };
   // dense item v: (b, h) major, query tiles of a head heaviest first under
   // a causal mask
-  auto dense_item = [&](const int v) {
-    const int bh = v / p.tiles_per_head;
-    const int rank = v - bh * p.tiles_per_head;
-    const int b = bh / p.H;
-    const int h = bh - b * p.H;
-    a_tile = CAUSAL ? p.tiles_per_head - 1 - rank : rank;
+  auto dense_at = [&](const int v) {
+    int b, h;
+    dense_item(v, p.tiles_per_head, p.H, CAUSAL, b, h, a_tile);
     a_sq = p.Sq;
     a_skv = p.Skv;
     a_off = p.Skv - p.Sq;
     const int kvh = h / p.group;
+    const int bh = b * p.H + h;
     if constexpr (BSHD) {  // [B, S, H, d]
       a_q0 = ((int64_t)b * p.Sq * p.H + h) * D;
       a_kv0 = ((int64_t)b * p.Skv * p.Hkv + kvh) * D;
@@ -502,18 +535,10 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     a_lse0 = (int64_t)bh * p.Sq;
     a_sink = sink_of(h);
   };
-  // bounds of varlen sequence bb, clamped into [0, T]
-  auto seq_bounds = [&](const int bb, int& s0, int& s1) {
-    const int T = p.Sq;
-    s0 = p.cu[bb];
-    s1 = p.cu[bb + 1];
-    s0 = s0 < 0 ? 0 : (s0 > T ? T : s0);
-    s1 = s1 < s0 ? s0 : (s1 > T ? T : s1);
-  };
   // query tile `tile` of head h in varlen sequence bb
   auto seq_item = [&](const int h, const int bb, const int tile) {
     int s0, s1;
-    seq_bounds(bb, s0, s1);
+    seq_bounds(p.cu, p.Sq, bb, s0, s1);
     a_tile = tile;
     a_sq = a_skv = s1 - s0;
     a_off = 0;
@@ -528,24 +553,13 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     a_lse0 = (int64_t)h * p.Sq + s0;
     a_sink = sink_of(h);
   };
-  // varlen item v: h major, then the concatenated tiles of the sequences,
-  // last first under a causal mask; false for items past the last tile
-  auto varlen_item = [&](const int v) {
-    const int h = v / p.tiles_per_head;
-    int vt = v - h * p.tiles_per_head;
-    if (CAUSAL) vt = p.tiles_per_head - 1 - vt;
-    int acc = 0;
-    for (int bb = 0; bb < p.B; ++bb) {
-      int s0, s1;
-      seq_bounds(bb, s0, s1);
-      const int nt = ceil_div(s1 - s0, BM);
-      if (vt < acc + nt) {
-        seq_item(h, bb, vt - acc);
-        return true;
-      }
-      acc += nt;
-    }
-    return false;
+  // dispatched varlen item v (h major, then the concatenated tiles of the
+  // sequences, last first under a causal mask); false past the last tile
+  auto varlen_at = [&](const int v) {
+    int h, bb, tile;
+    if (!varlen_item(p.cu, p.B, p.Sq, BM, p.tiles_per_head, CAUSAL, v, h, bb, tile)) return false;
+    seq_item(h, bb, tile);
+    return true;
   };
   // varlen persistent order: XCD x takes the heads [x H/8, (x+1) H/8) (the
   // query heads of one KV head stay on one L2); its items (sequence, tile,
@@ -580,7 +594,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   if (VARLEN && p.persist_c > 0) {
     for (int i = tid; i < p.B; i += NT) {
       int s0, s1;
-      seq_bounds(i, s0, s1);
+      seq_bounds(p.cu, p.Sq, i, s0, s1);
       seq_tiles[i] = ceil_div(s1 - s0, BM);
     }
     __syncthreads();
@@ -589,34 +603,28 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     v_tmax = wave_max(mx);
     v_items = (int64_t)tiles_at_or_above(0) * hpx;
   }
-  auto listed_item = [&](const int64_t f, const int x) {
-    // level t: cum(t+1) <= f < cum(t); cum falls as t grows
-    int lo = 0, hi = v_tmax - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((int64_t)tiles_at_or_above(mid) * hpx > f) {
-        lo = mid;
-      } else {
-        hi = mid - 1;
+  // the items of XCD x's list (attn_sched.h, listed_locate): cum(t) from
+  // the staged tile counts, the rank-th sequence with more than t tiles by a
+  // ballot over 64 sequences at a time
+  auto listed_at = [&](const int64_t f, const int x) {
+    auto cum = [&](const int t) { return (int64_t)tiles_at_or_above(t) * hpx; };
+    auto nth = [&](const int t, int rank) {
+      for (int i0 = 0; i0 < p.B; i0 += 64) {
+        const int i = i0 + lane;
+        const int ti = seq_tiles[i < p.B ? i : 0];  // every lane reads inside the array
+        uint64_t m = __ballot(i < p.B && ti > t);
+        const int n = __popcll(m);
+        if (rank < n) {
+          for (int k = 0; k < rank; ++k) m &= m - 1;
+          return i0 + __builtin_ctzll(m);
+        }
+        rank -= n;
       }
-    }
-    const int t = lo;
-    const int rr = (int)(f - (int64_t)tiles_at_or_above(t + 1) * hpx);
-    int rank = rr / hpx;
-    const int h = x * hpx + (rr - rank * hpx);
-    // the rank-th sequence (in index order) with more than t tiles
-    for (int i0 = 0; i0 < p.B; i0 += 64) {
-      const int i = i0 + lane;
-      const int ti = seq_tiles[i < p.B ? i : 0];  // every lane reads inside the array
-      uint64_t m = __ballot(i < p.B && ti > t);
-      const int n = __popcll(m);
-      if (rank < n) {
-        for (int k = 0; k < rank; ++k) m &= m - 1;
-        seq_item(h, i0 + __builtin_ctzll(m), t);
-        return;
-      }
-      rank -= n;
-    }
+      return 0;  // not reached for f < cum(0)
+    };
+    int seq, tile, head;
+    listed_locate(f, x, hpx, v_tmax, cum, nth, seq, tile, head);
+    seq_item(head, seq, tile);
   };
   // one workgroup per item (persist_c == 0), or a persistent grid of one
   // workgroup per CU (8 XCDs x persist_c).  Persistent workgroups take items
@@ -633,27 +641,23 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
       const int v = xcd_remap(blockIdx.x, p.work_items);
       if (v < 0) return false;
       if constexpr (VARLEN) {
-        skip = !varlen_item(v);
+        skip = !varlen_at(v);
       } else {
-        dense_item(v);
+        dense_at(v);
       }
       return true;
     }
     if constexpr (!VARLEN) {
-      const int C = p.persist_c;
-      const int x = blockIdx.x % 8, c = blockIdx.x / 8;
-      const int per = p.work_items / 8;
-      if (r * C >= per) return false;
-      dense_item(x * per + r * C + ((r & 1) ? C - 1 - c : c));
+      const int v = persist_dense_item(blockIdx.x, r, p.persist_c, p.work_items);
+      if (v < 0) return false;
+      dense_at(v);
     } else {
-      const int C = p.persist_c;
-      const int x = blockIdx.x % 8, c = blockIdx.x / 8;
-      if ((int64_t)r * C >= v_items) return false;
-      const int64_t f = (int64_t)r * C + ((r & 1) ? C - 1 - c : c);
-      if (f >= v_items) {
+      const int64_t f = persist_listed_index(blockIdx.x, r, p.persist_c, v_items);
+      if (f == -1) return false;
+      if (f < 0) {
         skip = true;
       } else {
-        listed_item(f, x);
+        listed_at(f, blockIdx.x % 8);
       }
     }
     return true;

@@ -99,9 +99,21 @@ typedef enum { ATTN_BHSD = 0, ATTN_BSHD = 1 } attn_layout;
 /* Largest split count the decode path accepts. */
 #define ATTN_MAX_SPLITS 256
 
+/* Kernel selection flags for attn_opts.flags (bf16 prefill only; every
+ * choice computes the same function, these exist to compare kernels and to
+ * test one path against another):
+ *   ATTN_FLAG_BASIC_PREFILL: run the basic tiled kernel (one wave group,
+ *     BHSD, no window or sink; ignored when a window, sinks or BSHD are
+ *     requested) instead of the two-group ping-pong kernel.
+ *   ATTN_FLAG_NO_PERSIST: one workgroup per query tile instead of the
+ *     persistent grid of one workgroup per CU (the result is bitwise the
+ *     same). */
+#define ATTN_FLAG_BASIC_PREFILL 1u
+#define ATTN_FLAG_NO_PERSIST 2u
+
 typedef struct {
-  /* Decode path only: 0 = library heuristic (or the ATTN_NUM_SPLITS
-   * environment variable when set), else 1 .. ATTN_MAX_SPLITS. */
+  /* Decode path only: 0 = library heuristic (attn_decode_num_splits), else
+   * 1 .. ATTN_MAX_SPLITS. */
   int num_splits;
   /* Decode path only: caller-provided device workspace of at least
    * attn_workspace_bytes(...) bytes, 256-byte aligned; NULL lets the library
@@ -109,6 +121,9 @@ typedef struct {
    * until this call's kernels on `stream` have finished. */
   void* workspace;
   size_t workspace_bytes;
+  /* ATTN_FLAG_* bits; 0 for the default kernels.  Unknown bits are
+   * ATTN_EINVAL. */
+  unsigned flags;
 } attn_opts;
 
 /* bf16 q, k, v, o; fp32 lse.  The path named by the pages: tiled forward for
@@ -212,7 +227,8 @@ attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cac
  * may be NULL) holds Delta and the LSE in log2 units, one fp32 per query row
  * each: attn_bwd_workspace_bytes(B, H, Sq) bytes (varlen: (1, H, T)),
  * 256-byte aligned, else it is allocated stream-ordered.  Validation, errors
- * and ordering on `stream` as for attn_fwd_ex; opts->num_splits is ignored. */
+ * and ordering on `stream` as for attn_fwd_ex; opts->num_splits and opts->flags
+ * are ignored. */
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                      void* dq, void* dk, void* dv, int B, int H, int Hkv, int Sq, int Skv, int d, float scale,
                      int causal, const int32_t* cu_seqlens, void* stream, const attn_opts* opts);
@@ -243,8 +259,9 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Sq);
  * Returns 0 for invalid sizes. */
 size_t attn_workspace_bytes(int B, int H, int d, int num_splits);
 
-/* The split count the decode path would use for these sizes when the caller
- * passes none (the ATTN_NUM_SPLITS environment variable is honoured). */
+/* The split count the decode path uses for these sizes when the caller
+ * passes none: enough splits of at least 256 keys for about 1024
+ * workgroups. */
 int attn_decode_num_splits(int B, int Hkv, int Skv);
 
 /* Static text for a status code. */

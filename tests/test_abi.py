@@ -70,6 +70,7 @@ def call(lib, *, q=P, k=P, v=P, o=Q2, lse=None, B=1, H=4, Hkv=2, Sq=8, Skv=8, d=
     (dict(dtype=7), ea.ATTN_EINVAL),
     (dict(opts=ea.AttnOpts(ea.ATTN_MAX_SPLITS + 1, None, 0)), ea.ATTN_EINVAL),
     (dict(opts=ea.AttnOpts(-1, None, 0)), ea.ATTN_EINVAL),
+    (dict(opts=ea.AttnOpts(0, None, 0, 4)), ea.ATTN_EINVAL),      # unknown flag bit
     # decode path with a caller workspace that is too small / misaligned
     (dict(Sq=1, Skv=100, opts=ea.AttnOpts(4, 0x500000, 16)), ea.ATTN_EINVAL),
     (dict(Sq=1, Skv=100, opts=ea.AttnOpts(4, 0x500010, 1 << 20)), ea.ATTN_EINVAL),
@@ -99,12 +100,12 @@ def test_workspace_bytes(lib):
 
 
 def test_decode_split_heuristic(lib, monkeypatch):
-    monkeypatch.delenv("ATTN_NUM_SPLITS", raising=False)
     assert ea.attn_decode_num_splits(32, 8, 16384) == 4      # 256 (b, kv-head) pairs -> 1024 workgroups
     assert ea.attn_decode_num_splits(1, 1, 100) == 1          # short caches are not split
     assert ea.attn_decode_num_splits(1, 8, 1 << 20) == 128
+    # no environment variable changes what the library does
     monkeypatch.setenv("ATTN_NUM_SPLITS", "16")
-    assert ea.attn_decode_num_splits(32, 8, 16384) == 16
+    assert ea.attn_decode_num_splits(32, 8, 16384) == 4
 
 
 def test_status_strings(lib):

@@ -23,7 +23,7 @@ import pytest
 from exact_attention_09_amd import synth
 from exact_attention_09_amd.workloads import WORKLOADS, host_f32, to_device
 from oracle import backward as bwd_oracle
-from test_parity_gpu import say
+from parity import say
 
 pytestmark = pytest.mark.gpu
 

@@ -1,24 +1,18 @@
 """GPU parity: the HIP path through the C ABI against the fp64 CPU oracle on
-the same seeded inputs.
-
-Bars: |dO| <= 1e-5 for fp32 inputs; for bf16 inputs the computation gets
-1e-2 and the final rounding of O to bf16 (the output format) is added on
-top: |dO| <= 1e-2 + half the bf16 spacing at the exact value (0.0039 or less
-for |O| < 2, 0.0078 for |O| in [2, 4)).  |dLSE| <= 1e-3.  Rows that see no
-key must give O = 0 and LSE = -inf exactly.  The printed max |dO| is the raw
-difference.
+the same seeded inputs (bars in ``parity.py``: the raw 1e-2 workload bar on
+every element of the benchmark workloads, the bf16 rounding bound everywhere,
+1e-5 for fp32, 1e-3 for the LSE).
 """
 
 import math
-import sys
 import zlib
 
 import numpy as np
 import pytest
 
-import oracle
 from exact_attention_09_amd import synth
-from exact_attention_09_amd.workloads import WORKLOADS, Workload, host_f32, to_device
+from exact_attention_09_amd.workloads import WORKLOADS, host_f32, to_device
+from parity import bf16_half_spacing, check, oracle_threads, reference, say
 from pins import assert_printed, golden
 
 pytestmark = pytest.mark.gpu
@@ -35,52 +29,20 @@ def gpu():
     return ea
 
 
-def say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
-
-
-def gpu_run(q, k, v, dtype, causal, scale, cu=None, num_splits=0):
+def gpu_run(q, k, v, dtype, causal, scale, cu=None, num_splits=0, flags=0):
     import exact_attention_09_amd as ea
     qt, kt, vt = (to_device(x, dtype) for x in (q, k, v))
     cut = torch.from_numpy(np.asarray(cu, np.int32)).cuda() if cu is not None else None
     o, lse = ea.attn_fwd_ex(qt, kt, vt, causal=causal, scale=scale, cu_seqlens=cut,
-                            num_splits=num_splits)
+                            num_splits=num_splits, flags=flags)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def bf16_half_spacing(x):
-    """Half the distance between adjacent bf16 values around |x|."""
-    ax = np.maximum(np.abs(x), 2.0 ** -126)
-    return 0.5 * 2.0 ** (np.floor(np.log2(ax)) - 7)
-
-
-def check(o, lse, o_ref, lse_ref, dtype, what=""):
-    o_ref = np.asarray(o_ref).reshape(o.shape)
-    lse_ref = np.asarray(lse_ref).reshape(lse.shape)
-    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
-    empty = np.isneginf(lse_ref)
-    assert np.array_equal(np.isneginf(lse), empty), f"{what}: -inf LSE pattern differs"
-    assert np.all(o[empty] == 0.0) if empty.any() else True
-    err = np.abs(o - o_ref)
-    if dtype == "f32":
-        tol = np.full_like(o_ref, 1e-5)
-    else:
-        tol = 1e-2 + bf16_half_spacing(o_ref)
-    worst = np.unravel_index(np.argmax(err - tol), err.shape)
-    assert np.all(err <= tol), (f"{what}: max |dO| {err.max():.3g} (at {worst}, ref {o_ref[worst]:.5g}, "
-                                f"got {o[worst]:.5g})")
-    fin = ~empty
-    lerr = np.abs(lse[fin] - lse_ref[fin]).max(initial=0.0)
-    assert lerr <= 1e-3, f"{what}: max |dLSE| {lerr:.3g}"
-    rounding = np.abs(o - o_ref).max(initial=0.0)
-    say(f"  {what}: max|dO|={rounding:.3g} max|dLSE|={lerr:.3g}")
-
-
 def oracle_dense(q, k, v, dtype, scale, causal, cu=None, rows=None):
-    return oracle.attention(host_f32(q, dtype), host_f32(k, dtype), host_f32(v, dtype), scale, causal,
-                            cu_seqlens=cu, rows=rows)
+    """(O, LSE, A) of the oracle for host inputs (bf16 bits or fp32)."""
+    return reference(host_f32(q, dtype), host_f32(k, dtype), host_f32(v, dtype), scale, causal,
+                     cu_seqlens=cu, rows=rows)
 
 
 # ------------------------------------------------------------ worked examples
@@ -112,8 +74,8 @@ def test_worked_examples_through_api(example, dtype, rows, num_splits):
         q, k, v = (synth.f32_to_bf16_bits(x) for x in (q, k, v))  # all values exact in bf16
     say(f"worked example {example} {dtype} rows={rows} splits={num_splits}")
     o, lse = gpu_run(q, k, v, dtype, False, 1.0, num_splits=num_splits)
-    o_ref, lse_ref = oracle_dense(q, k, v, dtype, 1.0, False)
-    check(o, lse, o_ref, lse_ref, dtype, f"{example}/{dtype}")
+    o_ref, lse_ref, a_ref = oracle_dense(q, k, v, dtype, 1.0, False)
+    check(o, lse, o_ref, lse_ref, dtype, f"{example}/{dtype}", a_ref=a_ref, workload=True)
     for r in range(rows):
         for j, w in enumerate(g["weights"]):
             got = o[0, 0, r, j]
@@ -128,63 +90,30 @@ def test_worked_examples_through_api(example, dtype, rows, num_splits):
 
 # ------------------------------------------------------------ the workloads
 
-SAMPLE_ROWS = 384
+# the benchmark workloads (the five configurations, the 8K one with and
+# without the causal mask), compared on every output element
+CONFIG_WORKLOADS = ["single_head_f32", "mha_causal_s2048_d64", "mha_s8192_d128", "mha_causal_s8192_d128",
+                    "varlen_gqa_causal_d128", "decode_gqa_s16384_d128"]
 
 
-def sample_rows(wl: Workload, rng):
-    """Rows for the oracle at full size: tile edges and random rows."""
-    if wl.varlen:
-        rows = []
-        for b, L in enumerate(wl.lengths):
-            for i in sorted({0, 1, 127, 128, L // 2, L - 2, L - 1}):
-                if 0 <= i < L:
-                    rows.append((b, int(rng.integers(wl.H)), i))
-        while len(rows) < SAMPLE_ROWS:
-            b = int(rng.integers(len(wl.lengths)))
-            rows.append((b, int(rng.integers(wl.H)), int(rng.integers(wl.lengths[b]))))
-        return np.array(rows, np.int64)
-    fixed = sorted({0, 1, 63, 64, 127, 128, 129, wl.Sq // 2, wl.Sq - 129, wl.Sq - 128, wl.Sq - 2, wl.Sq - 1})
-    rows = [(int(rng.integers(wl.B)), int(rng.integers(wl.H)), i) for i in fixed if 0 <= i < wl.Sq]
-    while len(rows) < SAMPLE_ROWS:
-        rows.append((int(rng.integers(wl.B)), int(rng.integers(wl.H)), int(rng.integers(wl.Sq))))
-    return np.array(rows, np.int64)
-
-
-def gather_rows(wl, o, lse, rows):
-    if wl.varlen:
-        cu = wl.cu_seqlens()
-        return (np.stack([o[0, h, cu[b] + i] for b, h, i in rows]),
-                np.array([lse[0, h, cu[b] + i] for b, h, i in rows]))
-    return (np.stack([o[b, h, i] for b, h, i in rows]), np.array([lse[b, h, i] for b, h, i in rows]))
-
-
-FULL_ORACLE = {"single_head_f32", "mha_causal_s2048_d64", "decode_gqa_s16384_d128"}
-
-
-@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if not (w.paged or w.backward)])
+@pytest.mark.parametrize("name", CONFIG_WORKLOADS)
 def test_workload_parity(name):
+    """Every row of the workload against the oracle: the raw 1e-2 bar (1e-5
+    for fp32) and the rounding bound on each element, 1e-3 on each LSE."""
     wl = WORKLOADS[name]
     say(f"workload {name}: B={wl.B} H={wl.H} Hkv={wl.Hkv} Sq={wl.Sq} Skv={wl.Skv} d={wl.d} "
-        f"{wl.dtype} causal={wl.causal}")
+        f"{wl.dtype} causal={wl.causal} (oracle on {oracle_threads()} threads)")
     x = wl.make_inputs()
     o, lse = gpu_run(x["q"], x["k"], x["v"], wl.dtype, wl.causal, wl.scale, cu=x["cu_seqlens"],
                      num_splits=wl.num_splits)
-    # properties at full size
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     vmax = float(np.abs(host_f32(x["v"], wl.dtype)).max())
     assert np.abs(o).max() <= vmax * (1 + 2 ** -7)  # a convex combination of V rows
-    if name in FULL_ORACLE:
-        o_ref, lse_ref = oracle_dense(x["q"], x["k"], x["v"], wl.dtype, wl.scale, wl.causal,
-                                      cu=x["cu_seqlens"])
-        check(o, lse, o_ref, lse_ref, wl.dtype, name)
-    else:
-        rows = sample_rows(wl, np.random.default_rng(wl.wid))
-        q, k, v = (host_f32(x[t], wl.dtype) for t in ("q", "k", "v"))
-        if wl.varlen:
-            q, k, v = q[0], k[0], v[0]
-        o_ref, lse_ref = oracle.attention(q, k, v, wl.scale, wl.causal, cu_seqlens=x["cu_seqlens"], rows=rows)
-        og, lg = gather_rows(wl, o, lse, rows)
-        check(og, lg, o_ref, lse_ref, wl.dtype, f"{name} ({len(rows)} sampled rows)")
+    q, k, v = (host_f32(x[t], wl.dtype) for t in ("q", "k", "v"))
+    if wl.varlen:
+        q, k, v, o, lse = q[0], k[0], v[0], o[0], lse[0]
+    o_ref, lse_ref, a_ref = reference(q, k, v, wl.scale, wl.causal, cu_seqlens=x["cu_seqlens"])
+    check(o, lse, o_ref, lse_ref, wl.dtype, name, a_ref=a_ref if wl.dtype == "bf16" else None, workload=True)
 
 
 # ------------------------------------------------------------ edge shapes
@@ -223,8 +152,8 @@ def test_edge_shapes(case):
     v = synth.normal_tensor(seed * 10 + 2, (B, Hkv, Skv, d), dtype)
     scale = 1.0 / math.sqrt(d)
     o, lse = gpu_run(q, k, v, dtype, causal, scale, num_splits=ns)
-    o_ref, lse_ref = oracle_dense(q, k, v, dtype, scale, causal)
-    check(o, lse, o_ref, lse_ref, dtype, str(case))
+    o_ref, lse_ref, a_ref = oracle_dense(q, k, v, dtype, scale, causal)
+    check(o, lse, o_ref, lse_ref, dtype, str(case), a_ref=a_ref)
 
 
 VARLEN_EDGE = [
@@ -251,11 +180,12 @@ def test_varlen_edges(case):
     o, lse = gpu_run(q, k, v, dtype, causal, scale, cu=cu)
     if T == 0:
         return
-    o_ref, lse_ref = oracle.attention(host_f32(q, dtype)[0], host_f32(k, dtype)[0], host_f32(v, dtype)[0],
+    o_ref, lse_ref, a_ref = reference(host_f32(q, dtype)[0], host_f32(k, dtype)[0], host_f32(v, dtype)[0],
                                       scale, causal, cu_seqlens=cu)
-    check(o[0], lse[0], o_ref, lse_ref, dtype, str(case))
+    check(o[0], lse[0], o_ref, lse_ref, dtype, str(case), a_ref=a_ref)
 
 
+BASIC_FLAG = 1  # ATTN_FLAG_BASIC_PREFILL
 BASIC = [
     ("dense", 1, 2, 2, 257, 257, True, 128),
     ("dense", 2, 4, 1, 77, 200, True, 128),
@@ -268,10 +198,9 @@ BASIC = [
 
 
 @pytest.mark.parametrize("case", BASIC, ids=lambda c: "-".join(map(str, c)))
-def test_basic_kernel(case, monkeypatch):
-    """bf16 prefill normally runs the ping-pong kernel; ATTN_BASIC_PREFILL
+def test_basic_kernel(case):
+    """bf16 prefill normally runs the ping-pong kernel; ATTN_FLAG_BASIC_PREFILL
     selects the basic tiled kernel, which must meet the same bar."""
-    monkeypatch.setenv("ATTN_BASIC_PREFILL", "1")
     say(f"basic kernel case {case}")
     seed = zlib.crc32(repr(case).encode()) % 10000
     d = case[-1]
@@ -281,27 +210,27 @@ def test_basic_kernel(case, monkeypatch):
         T = sum(lengths)
         cu = synth.cu_seqlens_from_lengths(lengths)
         q, k, v = (synth.normal_tensor(seed * 10 + i, (1, h, T, d), "bf16") for i, h in enumerate((H, Hkv, Hkv)))
-        o, lse = gpu_run(q, k, v, "bf16", causal, scale, cu=cu)
-        o_ref, lse_ref = oracle.attention(host_f32(q, "bf16")[0], host_f32(k, "bf16")[0],
+        o, lse = gpu_run(q, k, v, "bf16", causal, scale, cu=cu, flags=BASIC_FLAG)
+        o_ref, lse_ref, a_ref = reference(host_f32(q, "bf16")[0], host_f32(k, "bf16")[0],
                                           host_f32(v, "bf16")[0], scale, causal, cu_seqlens=cu)
-        check(o[0], lse[0], o_ref, lse_ref, "bf16", str(case))
+        check(o[0], lse[0], o_ref, lse_ref, "bf16", str(case), a_ref=a_ref)
         return
     _, B, H, Hkv, Sq, Skv, causal, _ = case
     q = synth.normal_tensor(seed * 10 + 0, (B, H, Sq, d), "bf16")
     k = synth.normal_tensor(seed * 10 + 1, (B, Hkv, Skv, d), "bf16")
     v = synth.normal_tensor(seed * 10 + 2, (B, Hkv, Skv, d), "bf16")
-    o, lse = gpu_run(q, k, v, "bf16", causal, scale)
-    o_ref, lse_ref = oracle_dense(q, k, v, "bf16", scale, causal)
-    check(o, lse, o_ref, lse_ref, "bf16", str(case))
+    o, lse = gpu_run(q, k, v, "bf16", causal, scale, flags=BASIC_FLAG)
+    o_ref, lse_ref, a_ref = oracle_dense(q, k, v, "bf16", scale, causal)
+    check(o, lse, o_ref, lse_ref, "bf16", str(case), a_ref=a_ref)
 
 
 @pytest.mark.parametrize("varlen", [False, True])
 @pytest.mark.parametrize("causal", [False, True])
-def test_dispatched_grid_matches_persistent(causal, varlen, monkeypatch):
+def test_dispatched_grid_matches_persistent(causal, varlen):
     """bf16 prefill runs a persistent grid when the query tiles divide evenly
     over the CUs (dense) or when the sequence scan is short (varlen); the
-    one-workgroup-per-tile grid (ATTN_NO_PERSIST) must give bitwise the same
-    result."""
+    one-workgroup-per-tile grid (ATTN_FLAG_NO_PERSIST) must give bitwise the
+    same result."""
     import exact_attention_09_amd as ea
     say(f"persistent vs dispatched, causal={causal} varlen={varlen}")
     d = 128
@@ -315,8 +244,7 @@ def test_dispatched_grid_matches_persistent(causal, varlen, monkeypatch):
         cu = None
         q, k, v = (to_device(synth.normal_tensor(9100 + i, (1, 32, 2048, d), "bf16"), "bf16") for i in range(3))
     o1, l1 = ea.attn_fwd(q, k, v, causal=causal, cu_seqlens=cu)
-    monkeypatch.setenv("ATTN_NO_PERSIST", "1")
-    o2, l2 = ea.attn_fwd(q, k, v, causal=causal, cu_seqlens=cu)
+    o2, l2 = ea.attn_fwd(q, k, v, causal=causal, cu_seqlens=cu, flags=ea.ATTN_FLAG_NO_PERSIST)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
@@ -352,10 +280,10 @@ def test_persistent_shapes(case):
     scale = 1.0 / math.sqrt(d)
     o, lse = gpu_run(q, k, v, "bf16", causal, scale)
     rows = _edge_and_random_rows(B, H, Sq, np.random.default_rng(seed))
-    o_ref, lse_ref = oracle_dense(q, k, v, "bf16", scale, causal, rows=rows)
+    o_ref, lse_ref, a_ref = oracle_dense(q, k, v, "bf16", scale, causal, rows=rows)
     og = np.stack([o[b, h, i] for b, h, i in rows])
     lg = np.array([lse[b, h, i] for b, h, i in rows])
-    check(og, lg, o_ref, lse_ref, "bf16", str(case))
+    check(og, lg, o_ref, lse_ref, "bf16", str(case), a_ref=a_ref)
 
 
 def test_persistent_varlen_many_sequences():
@@ -378,11 +306,11 @@ def test_persistent_varlen_many_sequences():
             if 0 <= i < L:
                 rows.append((b, int(rng.integers(H)), i))
     rows = np.array(rows, np.int64)
-    rf, lf = oracle.attention(host_f32(q, "bf16")[0], host_f32(k, "bf16")[0], host_f32(v, "bf16")[0],
-                              scale, True, cu_seqlens=cu, rows=rows)
+    rf, lf, af = reference(host_f32(q, "bf16")[0], host_f32(k, "bf16")[0], host_f32(v, "bf16")[0],
+                           scale, True, cu_seqlens=cu, rows=rows)
     og = np.stack([o[0, h, cu[b] + i] for b, h, i in rows])
     lg = np.array([lse[0, h, cu[b] + i] for b, h, i in rows])
-    check(og, lg, rf, lf, "bf16", "persistent varlen")
+    check(og, lg, rf, lf, "bf16", "persistent varlen", a_ref=af)
 
 
 # ------------------------------------------------------------ determinism, canaries

@@ -11,10 +11,9 @@ import zlib
 import numpy as np
 import pytest
 
-import oracle
 from exact_attention_09_amd import synth
 from exact_attention_09_amd.workloads import host_f32, to_device
-from test_parity_gpu import check, say
+from parity import check, reference, say
 
 pytestmark = pytest.mark.gpu
 
@@ -74,12 +73,12 @@ def test_bshd_dense(case):
         rng = np.random.default_rng(seed)
         rows = np.array([(int(rng.integers(B)), int(rng.integers(H)), i)
                          for i in [0, 1, 255, 256, 1023, 1024, 2047] + list(rng.integers(0, Sq, 120))], np.int64)
-    o_ref, lse_ref = oracle.attention(tr(q), tr(k), tr(v), 1.0 / math.sqrt(d), causal, rows=rows, window=w,
+    o_ref, lse_ref, a_ref = reference(tr(q), tr(k), tr(v), 1.0 / math.sqrt(d), causal, rows=rows, window=w,
                                       sinks=sinks)
     if rows is not None:
         og = np.stack([og[b, h, i] for b, h, i in rows])
         lg = np.array([lg[b, h, i] for b, h, i in rows])
-    check(og, lg, o_ref, lse_ref, "bf16", str(case))
+    check(og, lg, o_ref, lse_ref, "bf16", str(case), a_ref=a_ref)
 
 
 @pytest.mark.parametrize("causal,w", [(True, 0), (False, 0), (True, 64)])
@@ -103,6 +102,7 @@ def test_thd_varlen(causal, w):
     assert torch.equal(o.transpose(0, 1).contiguous().view(torch.int16), o2[0].view(torch.int16))
     assert torch.equal(lse, lse2[0])
     tr = lambda x: np.ascontiguousarray(host_f32(x, "bf16").transpose(1, 0, 2))
-    o_ref, lse_ref = oracle.attention(tr(q), tr(k), tr(v), 1.0 / math.sqrt(d), causal, cu_seqlens=cu, window=w)
+    o_ref, lse_ref, a_ref = reference(tr(q), tr(k), tr(v), 1.0 / math.sqrt(d), causal, cu_seqlens=cu, window=w)
     og = o.transpose(0, 1).float().cpu().numpy().astype(np.float64)
-    check(og, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", f"thd causal={causal} w={w}")
+    check(og, lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", f"thd causal={causal} w={w}",
+          a_ref=a_ref)

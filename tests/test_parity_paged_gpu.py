@@ -18,7 +18,7 @@ import pytest
 from exact_attention_09_amd import synth
 from exact_attention_09_amd.workloads import WORKLOADS, host_f32, to_device
 from oracle import paged as paged_oracle
-from test_parity_gpu import check, say
+from parity import check, say
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +57,8 @@ def test_paged_workload_parity_and_equals_contiguous():
     q32 = host_f32(x["q"], "bf16")[:, :, 0, :]
     kc, vc = host_f32(x["k"], "bf16"), host_f32(x["v"], "bf16")
     o_ref, lse_ref = paged_oracle.paged_attention(q32, kc, vc, x["block_table"], x["seqlens_k"], wl.scale)
-    check(og, lg, o_ref, lse_ref, "bf16", "paged decode workload")
+    a_ref, _ = paged_oracle.paged_attention(q32, kc, np.abs(vc), x["block_table"], x["seqlens_k"], wl.scale)
+    check(og, lg, o_ref, lse_ref, "bf16", "paged decode workload", a_ref=a_ref, workload=True)
     # the same keys laid out contiguously through the dense decode path
     kd = np.stack([paged_oracle.gather(x["k"], x["block_table"][b], wl.Skv) for b in range(wl.B)])
     vd = np.stack([paged_oracle.gather(x["v"], x["block_table"][b], wl.Skv) for b in range(wl.B)])
@@ -96,9 +97,10 @@ def test_paged_edges(case):
     o, lse = run_paged(q, kc, vc, table, seqlens, scale, ns)
     og = o.float().cpu().numpy().astype(np.float64)[:, :, 0, :]
     lg = lse.cpu().numpy().astype(np.float64)
-    o_ref, lse_ref = paged_oracle.paged_attention(host_f32(q, "bf16")[:, :, 0, :], host_f32(kc, "bf16"),
-                                                  host_f32(vc, "bf16"), table, seqlens, scale)
-    check(og, lg, o_ref, lse_ref, "bf16", str(case))
+    q32, k32, v32 = host_f32(q, "bf16")[:, :, 0, :], host_f32(kc, "bf16"), host_f32(vc, "bf16")
+    o_ref, lse_ref = paged_oracle.paged_attention(q32, k32, v32, table, seqlens, scale)
+    a_ref, _ = paged_oracle.paged_attention(q32, k32, np.abs(v32), table, seqlens, scale)
+    check(og, lg, o_ref, lse_ref, "bf16", str(case), a_ref=a_ref)
 
 
 def test_paged_malformed_table_stays_in_bounds():

@@ -15,10 +15,9 @@ import zlib
 import numpy as np
 import pytest
 
-import oracle
 from exact_attention_09_amd import synth
 from exact_attention_09_amd.workloads import host_f32, to_device
-from test_parity_gpu import check, say
+from parity import check, oracle_threads, reference, say
 
 pytestmark = pytest.mark.gpu
 
@@ -77,9 +76,9 @@ def test_window_sink_dense(case):
     sinks = sink_values(seed * 10 + 5, H) if with_sinks else None
     o, lse = run(q, k, v, w, sinks)
     scale = 1.0 / math.sqrt(d)
-    o_ref, lse_ref = oracle.attention(host_f32(q, "bf16"), host_f32(k, "bf16"), host_f32(v, "bf16"), scale, True,
+    o_ref, lse_ref, a_ref = reference(host_f32(q, "bf16"), host_f32(k, "bf16"), host_f32(v, "bf16"), scale, True,
                                       window=w, sinks=sinks)
-    check(o, lse, o_ref, lse_ref, "bf16", str(case))
+    check(o, lse, o_ref, lse_ref, "bf16", str(case), a_ref=a_ref)
 
 
 def test_window_sink_persistent_grid():
@@ -97,11 +96,11 @@ def test_window_sink_persistent_grid():
     rows = [(0, int(rng.integers(H)), i) for i in fixed]
     rows += [(0, int(rng.integers(H)), int(rng.integers(S))) for _ in range(150)]
     rows = np.array(rows, np.int64)
-    o_ref, lse_ref = oracle.attention(host_f32(q, "bf16"), host_f32(k, "bf16"), host_f32(v, "bf16"),
+    o_ref, lse_ref, a_ref = reference(host_f32(q, "bf16"), host_f32(k, "bf16"), host_f32(v, "bf16"),
                                       1.0 / math.sqrt(d), True, rows=rows, window=w, sinks=sinks)
     og = np.stack([o[b, h, i] for b, h, i in rows])
     lg = np.array([lse[b, h, i] for b, h, i in rows])
-    check(og, lg, o_ref, lse_ref, "bf16", "persistent window/sink")
+    check(og, lg, o_ref, lse_ref, "bf16", "persistent window/sink", a_ref=a_ref)
 
 
 @pytest.mark.parametrize("w,with_sinks", [(100, True), (1, False), (0, True)])
@@ -116,9 +115,9 @@ def test_window_sink_varlen(w, with_sinks):
     v = synth.normal_tensor(7402, (1, Hkv, T, d), "bf16")
     sinks = sink_values(7405, H) if with_sinks else None
     o, lse = run(q, k, v, w, sinks, cu=cu)
-    o_ref, lse_ref = oracle.attention(host_f32(q, "bf16")[0], host_f32(k, "bf16")[0], host_f32(v, "bf16")[0],
+    o_ref, lse_ref, a_ref = reference(host_f32(q, "bf16")[0], host_f32(k, "bf16")[0], host_f32(v, "bf16")[0],
                                       1.0 / math.sqrt(d), True, cu_seqlens=cu, window=w, sinks=sinks)
-    check(o[0], lse[0], o_ref, lse_ref, "bf16", f"varlen w={w}")
+    check(o[0], lse[0], o_ref, lse_ref, "bf16", f"varlen w={w}", a_ref=a_ref)
 
 
 DECODE = [
@@ -141,9 +140,9 @@ def test_window_sink_decode(case):
     v = synth.normal_tensor(seed * 10 + 2, (B, Hkv, Skv, d), "bf16")
     sinks = sink_values(seed * 10 + 5, H) if with_sinks else None
     o, lse = run(q, k, v, w, sinks, num_splits=ns)
-    o_ref, lse_ref = oracle.attention(host_f32(q, "bf16"), host_f32(k, "bf16"), host_f32(v, "bf16"),
+    o_ref, lse_ref, a_ref = reference(host_f32(q, "bf16"), host_f32(k, "bf16"), host_f32(v, "bf16"),
                                       1.0 / math.sqrt(d), True, window=w, sinks=sinks)
-    check(o, lse, o_ref, lse_ref, "bf16", str(case))
+    check(o, lse, o_ref, lse_ref, "bf16", str(case), a_ref=a_ref)
 
 
 @pytest.mark.parametrize("Sq", [1, 700])
@@ -171,21 +170,14 @@ def test_neutral_window_and_sinks_are_causal(Sq):
 
 def test_swa_workload_parity():
     """The long-context window/sink workload at full size (32K tokens, window
-    4096, GQA) against the oracle on sampled rows, tile and band edges
-    included."""
+    4096, GQA, per-head sinks) against the oracle on every row."""
     from exact_attention_09_amd.workloads import WORKLOADS
     wl = WORKLOADS["swa_sink_s32768_d128"]
-    say(f"workload {wl.name}: H={wl.H} Hkv={wl.Hkv} S={wl.Sq} d={wl.d} window={wl.window}")
+    say(f"workload {wl.name}: H={wl.H} Hkv={wl.Hkv} S={wl.Sq} d={wl.d} window={wl.window} "
+        f"(oracle on {oracle_threads()} threads)")
     x = wl.make_inputs()
     o, lse = run(x["q"], x["k"], x["v"], wl.window, x["sinks"])
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    rng = np.random.default_rng(wl.wid)
-    fixed = [0, 1, 255, 256, 4095, 4096, 4097, 8191, 8192, 16384, 32766, 32767]
-    rows = [(0, int(rng.integers(wl.H)), i) for i in fixed]
-    rows += [(0, int(rng.integers(wl.H)), int(rng.integers(wl.Sq))) for _ in range(200)]
-    rows = np.array(rows, np.int64)
-    o_ref, lse_ref = oracle.attention(host_f32(x["q"], "bf16"), host_f32(x["k"], "bf16"), host_f32(x["v"], "bf16"),
-                                      wl.scale, True, rows=rows, window=wl.window, sinks=x["sinks"])
-    og = np.stack([o[b, h, i] for b, h, i in rows])
-    lg = np.array([lse[b, h, i] for b, h, i in rows])
-    check(og, lg, o_ref, lse_ref, "bf16", f"{wl.name} ({len(rows)} sampled rows)")
+    o_ref, lse_ref, a_ref = reference(host_f32(x["q"], "bf16"), host_f32(x["k"], "bf16"), host_f32(x["v"], "bf16"),
+                                      wl.scale, True, window=wl.window, sinks=x["sinks"])
+    check(o, lse, o_ref, lse_ref, "bf16", wl.name, a_ref=a_ref)
