@@ -10,7 +10,8 @@ Names mirror the C entry points:
 
 * ``attn_fwd`` (bf16), ``attn_fwd_f32`` (fp32), ``attn_fwd_ex`` (either, with
   split-KV options) take torch tensors on the GPU in BHSD layout and return
-  ``(o, lse)``;
+  ``(o, lse)``; ``attn_fwd_noalloc`` is ``attn_fwd_ex`` for callers that
+  cannot allocate (decode partials in a static per-GPU scratch array);
 * ``attn_fwd_window_sink`` is causal attention with a sliding window and/or
   per-head attention sinks;
 * ``attn_fwd_layout`` is the general bf16 call: BHSD or BSHD (packed THD for
@@ -37,7 +38,9 @@ ATTN_BF16, ATTN_F32 = 0, 1
 ATTN_BHSD, ATTN_BSHD = 0, 1
 ATTN_MAX_SPLITS = 256
 
-EXPORTED = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_window_sink", "attn_fwd_layout",
+ATTN_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+EXPORTED = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_noalloc", "attn_fwd_window_sink", "attn_fwd_layout",
             "attn_fwd_paged", "attn_bwd", "attn_bwd_window_sink", "attn_bwd_workspace_bytes", "attn_workspace_bytes",
             "attn_decode_num_splits", "attn_status_string", "attn_last_error")
 
@@ -77,6 +80,8 @@ def load_library(path: str = LIB_PATH):
         fn.argtypes = fwd_args
     lib.attn_fwd_ex.restype = ctypes.c_int
     lib.attn_fwd_ex.argtypes = fwd_args + [ctypes.c_int, ctypes.POINTER(AttnOpts)]
+    lib.attn_fwd_noalloc.restype = ctypes.c_int
+    lib.attn_fwd_noalloc.argtypes = fwd_args + [ctypes.c_int, ctypes.POINTER(AttnOpts)]
     lib.attn_fwd_window_sink.restype = ctypes.c_int
     lib.attn_fwd_window_sink.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
         ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(AttnOpts)]
@@ -191,6 +196,39 @@ def attn_fwd_ex(q, k, v, o=None, lse=None, *, causal: bool = False, scale: float
     st = lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Sq, Skv, d,
                          float(scale), int(bool(causal)), _ptr(cu_seqlens), ctypes.c_void_p(stream),
                          int(dtype), ctypes.byref(opts))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_last_error())
+    return o, lse
+
+
+def attn_fwd_noalloc(q, k, v, o, lse, *, causal: bool = False, scale: float | None = None, cu_seqlens=None,
+                     stream=None, dtype: int | None = None, num_splits: int = 0, flags: int = 0):
+    """``attn_fwd_ex`` through ``attn_fwd_noalloc``: the library allocates
+    nothing (decode partials in its static per-GPU scratch array).  The
+    caller passes the outputs ``o`` and ``lse`` (``lse`` may be None)."""
+    import torch
+    lib = load_library()
+    B, H, Hkv, Sq, Skv, d, dk = _shapes(q, k, cu_seqlens)
+    if dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must have the shape [.., Hkv, Skv, d] with q's d")
+    if dtype is None:
+        dtype = {torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}.get(q.dtype)
+        if dtype is None:
+            raise ValueError(f"unsupported dtype {q.dtype}")
+    want = torch.bfloat16 if dtype == ATTN_BF16 else torch.float32
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.dtype != want or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous {want} tensor on the GPU")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise ValueError("cu_seqlens must be an int32 tensor on the GPU")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    opts = AttnOpts(int(num_splits), None, 0, int(flags))
+    st = lib.attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Sq, Skv, d,
+                              float(scale), int(bool(causal)), _ptr(cu_seqlens), ctypes.c_void_p(stream),
+                              int(dtype), ctypes.byref(opts))
     if st != ATTN_OK:
         raise AttnError(st, attn_last_error())
     return o, lse

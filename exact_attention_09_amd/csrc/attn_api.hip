@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "attn.h"
 #include "attn_common.h"
@@ -64,6 +65,35 @@ static int device_cus() {
   return n;
 }
 
+// ---- the scratch memory of attn_fwd_noalloc: a static device array of
+// ATTN_NOALLOC_SCRATCH_BYTES, one copy per GPU (loaded with the library's
+// code object), holding the split-KV partials of the decode path.  Host code
+// uses it only through the device address hipGetSymbolAddress returns for
+// the current device (the array's name is a host-side stand-in).
+constexpr size_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The current device's address of the scratch array, looked up once per
+// device (with that device current) and kept.
+static attn_status scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_EUNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || a == nullptr) return hip_fail(e, "hipGetSymbolAddress of the scratch array");
+    addr[dev] = a;
+  }
+  *out = addr[dev];
+  return ATTN_OK;
+}
+
 extern "C" {
 
 const char* attn_status_string(attn_status s) {
@@ -96,7 +126,7 @@ namespace {
 attn_status forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
                     int Sq, int Skv, int d, float scale, int causal, const int32_t* cu_seqlens, void* stream,
                     attn_dtype dtype, const attn_opts* opts, int window, const float* sinks,
-                    attn_layout layout) {
+                    attn_layout layout, bool use_scratch = false) {
   g_err[0] = '\0';
   // ---- validation: no HIP call until every check has passed
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return fail(ATTN_EINVAL, "unknown dtype %d", (int)dtype);
@@ -198,7 +228,16 @@ attn_status forward(const void* q, const void* k, const void* v, void* o, float*
   const long rows = (long)B * H;
   void* ws = nullptr;
   bool own = false;
-  if (opts != nullptr && opts->workspace != nullptr) {
+  if (use_scratch) {
+    // attn_fwd_noalloc: the static scratch array, never an allocation
+    if (need > kScratchBytes)
+      return fail(ATTN_EINVAL,
+                  "the split partials need %zu bytes (B=%d H=%d d=%d splits=%d), more than the %zu bytes of "
+                  "scratch attn_fwd_noalloc holds (ATTN_NOALLOC_SCRATCH_BYTES); use fewer splits or attn_fwd_ex",
+                  need, B, H, d, splits, kScratchBytes);
+    const attn_status sst = scratch_address(&ws);
+    if (sst != ATTN_OK) return sst;
+  } else if (opts != nullptr && opts->workspace != nullptr) {
     if (opts->workspace_bytes < need)
       return fail(ATTN_EINVAL, "workspace of %zu bytes, %zu needed", opts->workspace_bytes, need);
     if (!aligned(opts->workspace, kWsAlign)) return fail(ATTN_EINVAL, "workspace must be 256-byte aligned");
@@ -239,6 +278,16 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
                         const attn_opts* opts) {
   return forward(q, k, v, o, lse, B, H, Hkv, Sq, Skv, d, scale, causal, cu_seqlens, stream, dtype, opts, 0,
                  nullptr, ATTN_BHSD);
+}
+
+attn_status attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                             int Hkv, int Sq, int Skv, int d, float scale, int causal, const int32_t* cu_seqlens,
+                             void* stream, attn_dtype dtype, const attn_opts* opts) {
+  g_err[0] = '\0';
+  if (opts != nullptr && opts->workspace != nullptr)
+    return fail(ATTN_EINVAL, "attn_fwd_noalloc takes no workspace (it uses its static scratch array)");
+  return forward(q, k, v, o, lse, B, H, Hkv, Sq, Skv, d, scale, causal, cu_seqlens, stream, dtype, opts, 0,
+                 nullptr, ATTN_BHSD, /*use_scratch=*/true);
 }
 
 attn_status attn_fwd_window_sink(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

@@ -64,7 +64,8 @@
  * no pointer after the call returns.  The only memory the library allocates
  * is the split-KV workspace of the decode path when the caller passes none,
  * taken and released stream-ordered (hipMallocAsync / hipFreeAsync) on
- * `stream`.
+ * `stream`; besides, its code object holds the static scratch array of
+ * attn_fwd_noalloc (ATTN_NOALLOC_SCRATCH_BYTES per GPU).
  *
  * `stream` is a hipStream_t; NULL means the default stream.
  */
@@ -142,6 +143,32 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
                         int H, int Hkv, int Sq, int Skv, int d, float scale, int causal,
                         const int32_t* cu_seqlens, void* stream, attn_dtype dtype,
                         const attn_opts* opts);
+
+/* Bytes of scratch memory attn_fwd_noalloc holds per GPU (16 MiB: the split
+ * partials of decode with B * H * splits * (d + 1) * 4 bytes up to that, e.g.
+ * B = 32, H = 32, d = 128, 16 splits takes 8.5 MB). */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* attn_fwd_ex without any device allocation, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments and results as attn_fwd_ex (bf16 or
+ * fp32, dense or varlen, prefill or split-KV decode); opts (may be NULL)
+ * gives num_splits and flags, and its workspace must be NULL (ATTN_EINVAL
+ * otherwise).  The decode path (dense Sq == 1) keeps its split partials in a
+ * library-owned static device array of ATTN_NOALLOC_SCRATCH_BYTES on each
+ * GPU, held until the process ends, instead of a workspace; a call whose
+ * partials need more (attn_workspace_bytes(B, H, d, splits) bytes) is
+ * rejected with ATTN_EINVAL before anything is launched.  The prefill path
+ * uses no scratch memory.  Every call on a GPU shares that GPU's array: two
+ * calls that may run at the same time on one GPU (streams not ordered by the
+ * caller) race on it, so order them on one stream or with events.  The split
+ * kernel writes every partial the combine reads, so nothing carries over
+ * from an earlier call.  The array's device address is looked up once per
+ * device, at the first decode call made with that device current.  No
+ * hipMalloc, hipFree or allocating library routine is called. */
+attn_status attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                             int Hkv, int Sq, int Skv, int d, float scale, int causal, const int32_t* cu_seqlens,
+                             void* stream, attn_dtype dtype, const attn_opts* opts);
 
 /* Causal attention with a sliding window and/or attention sinks, bf16.
  * Same arguments and layouts as attn_fwd (dense or varlen), always causal
