@@ -17,7 +17,18 @@
 //     group A, waves 4-7 group B; wave w and wave w+4 share a SIMD.
 //   * Time is cut into slots by workgroup barriers.  In every slot one group
 //     runs its matrix phase while the other runs its vector phase; group B
-//     runs one slot behind group A, so the roles alternate every slot.
+//     runs one slot behind group A, so the roles alternate every slot.  Each
+//     group runs its own copy of the slot sequence, so the role of every
+//     slot is fixed in the code rather than tested at run time.
+//   * Per-wave checks (is the tile computed, masked, the split tile) are
+//     hoisted out of the loop: each wave's "steady" tiles, which it computes
+//     whole with no key masked for any of its rows, form one range, and at
+//     d = 128 (outside the window variant) the slot loop is split around it,
+//     so a steady slot pair runs without any test.  Matrix phases inside an
+//     item always run both products: a wave that does not compute a tile
+//     holds P~ = 0 for it, so that tile's P~V adds nothing (K and V values
+//     are assumed finite, as the masked keys of a partial tile already
+//     require: 0 times a non-finite V would spread into the row).
 //   * Each wave keeps a single S tile in registers (32 rows x 64 keys), so the
 //     register footprint is that of the plain loop (2 waves per SIMD).
 //   * K/V tiles (64 keys) live in a ring of PF + 2 LDS stages of 32 KB.  A
@@ -53,6 +64,8 @@
 //   * Attention sink (tutorial sections 4.6 and 4.7): in the epilogue the
 //     sink's exp2(sink log2(e) - m*) joins the denominator, with
 //     m* = max(m scale', sink log2(e)) so that a large sink cannot overflow.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_internal.h"
 
@@ -256,223 +269,407 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  const int nslots = 2 * ntl + 2;
-  for (int slot = 0; slot < nslots; ++slot) {
-    // Tile k+PF is fetched into the stage of tile k+PF-STAGES, whose last
-    // read (its V, by group B) was in slot 2k-1: its V blocks by group B in
-    // slot 2k, its K blocks by group A in slot 2k+1, in both cases at the
-    // start of the loading group's vector phase.  (Loads issued by a wave
-    // that is about to run its matrix phase delay that phase's MFMAs, and a
-    // burst from all eight waves at once delays both phases: measured.)
-    if (((slot & 1) == 1) == (wu < 4)) {
-      const int k = slot >> 1;
-      if (k + PF < ntl) load_tile(k + PF);
+  // The two phases of a slot for tile t (relative index): matrix = P~V of
+  // tile t-1 and S^T of tile t, vector = mask, exponentials and row sums of
+  // tile t.
+  //
+  // Matrix phase inside an item: both products, unconditionally (a wave
+  // that did not compute tile t-1 holds P~ = 0, so its product adds nothing;
+  // an S^T of a tile it does not compute is never read).
+  auto matrix_steady = [&](const int t) {
+    // the matrix phase issues first on this SIMD; the other group's
+    // vector work fills the issue slots the MFMAs leave free
+    __builtin_amdgcn_s_setprio(ATTN_PP_PRIO);
+    const unsigned char* vb = smem + ((t + STAGES - 1) % STAGES) * STAGE_B + v_lane;
+    const unsigned char* kb = smem + (t % STAGES) * STAGE_B + k_lane;
+    // fragment (c, kbi) of K and (kc, db) of V, block offsets as immediates
+    auto vfrag = [&](int kc, int db) {
+      const unsigned char* a = vb + (NDB * kc + db) * 1024;
+      return join_tr(lds_read_tr16(a), lds_read_tr16(a + 512));
+    };
+    auto kfrag = [&](int c, int kbi) { return *(const bf16x8*)(kb + (NDC * kbi + c) * 1024); };
+    // the 16 P~V and 16 QK^T MFMAs are independent, so they are issued
+    // alternately, each with its operand read a few MFMAs ahead
+    {
+      if constexpr (LOCAL) {
+        // The same order written out MFMA pair by MFMA pair, each operand
+        // read AHEAD pairs earlier into a register ring, and fenced with
+        // sched_barrier.  In this instantiation the scheduler drops the
+        // sched_group_barrier pins below (every read then waited for
+        // lgkmcnt(0) before its MFMA: 23-29 % slower); where the pins hold,
+        // they are 0.5-1.5 % faster than this form.
+        constexpr int AH = ATTN_PP_AHEAD;
+        constexpr int R = AH + 1;
+        bf16x8 vr[R], kr[R];
+#pragma unroll
+        for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = f32x16{};
+        static_for<AH>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          vr[i] = vfrag(i / NDB, i % NDB);
+          kr[i] = kfrag(i / NKB, i % NKB);
+        });
+        static_for<NPV>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          constexpr int kc = i / NDB, db = i % NDB;
+          oacc[db] = mfma32(vr[i % R], pb[kc], oacc[db]);
+          if constexpr (i + AH < NPV) vr[(i + AH) % R] = vfrag((i + AH) / NDB, (i + AH) % NDB);
+          constexpr int c = i / NKB, kbi = i % NKB;
+          s[kbi] = mfma32(kr[i % R], qf[c], s[kbi]);
+          if constexpr (i + AH < NPV) kr[(i + AH) % R] = kfrag((i + AH) / NKB, (i + AH) % NKB);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else {
+        // (order pinned with sched_group_barrier: 0x100 LDS read, 0x008
+        // MFMA)
+#pragma unroll
+        for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = f32x16{};
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+          const int kc = i / NDB, db = i % NDB;
+          oacc[db] = mfma32(vfrag(kc, db), pb[kc], oacc[db]);
+          const int c = i / NKB, kbi = i % NKB;
+          s[kbi] = mfma32(kfrag(c, kbi), qf[c], s[kbi]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 3 * ATTN_PP_AHEAD, 0);
+#pragma unroll
+        for (int i = 0; i < NPV - ATTN_PP_AHEAD; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * ATTN_PP_AHEAD, 0);
+      }
     }
-
-    const int ls = slot - grp;  // this group's own slot index
-    if (ls >= 0) {
-      const int t = ls >> 1;
-      if ((ls & 1) == 0) {
-        // matrix phase: P~V of tile t-1, then S^T of tile t.  Operand
-        // fragments are double buffered in registers: the LDS reads of step
-        // i+1 are in flight while the MFMAs of step i run.
-        const bool do_pv = computes(t - 1) && !precise(t - 1);
-        const bool do_qk = computes(t);
-        // the matrix phase issues first on this SIMD; the other group's
-        // vector work fills the issue slots the MFMAs leave free
-        __builtin_amdgcn_s_setprio(ATTN_PP_PRIO);
-        const unsigned char* vb = smem + ((t + STAGES - 1) % STAGES) * STAGE_B + v_lane;
-        const unsigned char* kb = smem + (t % STAGES) * STAGE_B + k_lane;
-        // fragment (c, kbi) of K and (kc, db) of V, block offsets as immediates
-        auto vfrag = [&](int kc, int db) {
-          const unsigned char* a = vb + (NDB * kc + db) * 1024;
-          return join_tr(lds_read_tr16(a), lds_read_tr16(a + 512));
-        };
-        auto kfrag = [&](int c, int kbi) { return *(const bf16x8*)(kb + (NDC * kbi + c) * 1024); };
-        if (do_pv && do_qk) {
-          // steady state: the 16 P~V and 16 QK^T MFMAs are independent, so
-          // they are issued alternately, each with its operand read a few
-          // MFMAs ahead
-          if constexpr (LOCAL) {
-            // The same order written out MFMA pair by MFMA pair, each operand
-            // read AHEAD pairs earlier into a register ring, and fenced with
-            // sched_barrier.  In this instantiation the scheduler drops the
-            // sched_group_barrier pins below (every read then waited for
-            // lgkmcnt(0) before its MFMA: 23-29 % slower); where the pins hold,
-            // they are 0.5-1.5 % faster than this form.
-            constexpr int AH = ATTN_PP_AHEAD;
-            constexpr int R = AH + 1;
-            bf16x8 vr[R], kr[R];
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // First and last matrix phases of an item (S^T of tile 0 only, P~V of the
+  // last tile only), each as the wave computes it; the operand reads of one
+  // step are double buffered in registers, in flight during the MFMAs of the
+  // step before.
+  auto matrix_edge = [&](const int t, const bool do_pv, const bool do_qk) {
+    // the matrix phase issues first on this SIMD; the other group's
+    // vector work fills the issue slots the MFMAs leave free
+    __builtin_amdgcn_s_setprio(ATTN_PP_PRIO);
+    const unsigned char* vb = smem + ((t + STAGES - 1) % STAGES) * STAGE_B + v_lane;
+    const unsigned char* kb = smem + (t % STAGES) * STAGE_B + k_lane;
+    // fragment (c, kbi) of K and (kc, db) of V, block offsets as immediates
+    auto vfrag = [&](int kc, int db) {
+      const unsigned char* a = vb + (NDB * kc + db) * 1024;
+      return join_tr(lds_read_tr16(a), lds_read_tr16(a + 512));
+    };
+    auto kfrag = [&](int c, int kbi) { return *(const bf16x8*)(kb + (NDC * kbi + c) * 1024); };
+    {
+    bf16x8 kf[2][NKB];
+    if (do_pv) {
+      bf16x8 vf[2][NDB];
 #pragma unroll
-            for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = f32x16{};
-            static_for<AH>([&](auto ic) {
-              constexpr int i = decltype(ic)::value;
-              vr[i] = vfrag(i / NDB, i % NDB);
-              kr[i] = kfrag(i / NKB, i % NKB);
-            });
-            static_for<NPV>([&](auto ic) {
-              constexpr int i = decltype(ic)::value;
-              constexpr int kc = i / NDB, db = i % NDB;
-              oacc[db] = mfma32(vr[i % R], pb[kc], oacc[db]);
-              if constexpr (i + AH < NPV) vr[(i + AH) % R] = vfrag((i + AH) / NDB, (i + AH) % NDB);
-              constexpr int c = i / NKB, kbi = i % NKB;
-              s[kbi] = mfma32(kr[i % R], qf[c], s[kbi]);
-              if constexpr (i + AH < NPV) kr[(i + AH) % R] = kfrag((i + AH) / NKB, (i + AH) % NKB);
-              __builtin_amdgcn_sched_barrier(0);
-            });
-          } else {
-            // (order pinned with sched_group_barrier: 0x100 LDS read, 0x008
-            // MFMA)
+      for (int db = 0; db < NDB; ++db) vf[0][db] = vfrag(0, db);
 #pragma unroll
-            for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = f32x16{};
+      for (int kc = 0; kc < NKC; ++kc) {
+        if (kc + 1 < NKC) {
 #pragma unroll
-            for (int i = 0; i < NPV; ++i) {
-              const int kc = i / NDB, db = i % NDB;
-              oacc[db] = mfma32(vfrag(kc, db), pb[kc], oacc[db]);
-              const int c = i / NKB, kbi = i % NKB;
-              s[kbi] = mfma32(kfrag(c, kbi), qf[c], s[kbi]);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 3 * ATTN_PP_AHEAD, 0);
-#pragma unroll
-            for (int i = 0; i < NPV - ATTN_PP_AHEAD; ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * ATTN_PP_AHEAD, 0);
-          }
-        } else {
-        bf16x8 kf[2][NKB];
-        if (do_pv) {
-          bf16x8 vf[2][NDB];
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) vf[0][db] = vfrag(0, db);
-#pragma unroll
-          for (int kc = 0; kc < NKC; ++kc) {
-            if (kc + 1 < NKC) {
-#pragma unroll
-              for (int db = 0; db < NDB; ++db) vf[(kc + 1) & 1][db] = vfrag(kc + 1, db);
-            } else if (do_qk) {
-#pragma unroll
-              for (int kbi = 0; kbi < NKB; ++kbi) kf[0][kbi] = kfrag(0, kbi);
-            }
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(vf[kc & 1][db], pb[kc], oacc[db]);
-          }
+          for (int db = 0; db < NDB; ++db) vf[(kc + 1) & 1][db] = vfrag(kc + 1, db);
         } else if (do_qk) {
 #pragma unroll
           for (int kbi = 0; kbi < NKB; ++kbi) kf[0][kbi] = kfrag(0, kbi);
         }
-        if (do_qk) {
 #pragma unroll
-          for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = f32x16{};
+        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(vf[kc & 1][db], pb[kc], oacc[db]);
+      }
+    } else if (do_qk) {
 #pragma unroll
-          for (int c = 0; c < NDC; ++c) {
-            if (c + 1 < NDC) {
+      for (int kbi = 0; kbi < NKB; ++kbi) kf[0][kbi] = kfrag(0, kbi);
+    }
+    if (do_qk) {
 #pragma unroll
-              for (int kbi = 0; kbi < NKB; ++kbi) kf[(c + 1) & 1][kbi] = kfrag(c + 1, kbi);
-            }
+      for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = f32x16{};
 #pragma unroll
-            for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = mfma32(kf[c & 1][kbi], qf[c], s[kbi]);
-          }
+      for (int c = 0; c < NDC; ++c) {
+        if (c + 1 < NDC) {
+#pragma unroll
+          for (int kbi = 0; kbi < NKB; ++kbi) kf[(c + 1) & 1][kbi] = kfrag(c + 1, kbi);
         }
-        }
-        __builtin_amdgcn_s_setprio(0);
-      } else if (computes(t)) {
-        // vector phase for tile t
-        const int k0 = (t_first + t) * BN;
-        const bool partial = (k0 + BN > skv) || (CAUSAL && (k0 + BN - 1 > qw0 + off)) ||
-                             (W > 0 && k0 < qw0 + 31 + off - W + 1);
-        if (partial) {
 #pragma unroll
-          for (int kbi = 0; kbi < NKB; ++kbi)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {  // key = k0 + 32kbi + 8(r/4) + 4hh + r%4
-              const int kk = k0 + 32 * kbi + 8 * (r >> 2) + (r & 3);
-              if (kk >= lim_h || (LOCAL && kk < lo_h)) s[kbi][r] = -INFINITY;
-            }
-        }
-        // P~ against the current reference, S kept; this lane's share of the
-        // row sum as four independent chains
-        auto expo = [&]() {
-          float rp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int kc = 0; kc < NKC; ++kc) {
-            const f32x16& sk = s[kc >> 1];
-            const int rb = 8 * (kc & 1);
-            float e[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              e[j] = fast_exp2(fmaf(sk[rb + j], sl2, neg_ms));
-              rp[j & 3] += e[j];
-            }
-            pb[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-          }
-          return (rp[0] + rp[1]) + (rp[2] + rp[3]);
-        };
-        float ps = expo();
-        // a share above 2^8 means some P~ above 2^8, and a row without a
-        // reference has no P~ yet: exact reference update, then P~ again
-        if (__any(ps > kSumCap || m_used == -INFINITY)) {
-          float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-          for (int kbi = 0; kbi < NKB; ++kbi)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[kbi][r]);
-          const float mx = pair32_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
-          const float m_new = fmaxf(m_used, mx);
-          const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2((m_used - m_new) * sl2);
-          l_part *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-          m_used = m_new;
-          neg_ms = (m_used == -INFINITY) ? 0.0f : -m_used * sl2;
-          ps = expo();
-        }
-        l_part += ps;
-        if (precise(t)) {
-          // the split P~V product of this tile (V of tile t is in stage
-          // t % STAGES); the fp32 P~ is recomputed with expo()'s
-          // instructions, so its bf16 part is pb exactly
-          const unsigned char* vb = smem + (t % STAGES) * STAGE_B + v_lane;
-#pragma unroll
-          for (int kc = 0; kc < NKC; ++kc) {
-            const f32x16& sk = s[kc >> 1];
-            const int rb = 8 * (kc & 1);
-            float lo[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) lo[j] = fast_exp2(fmaf(sk[rb + j], sl2, neg_ms)) - (float)pb[kc][j];
-            const bf16x8 pl = to_bf16x8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-              const unsigned char* a = vb + (NDB * kc + db) * 1024;
-              const bf16x8 vf = join_tr(lds_read_tr16(a), lds_read_tr16(a + 512));
-              oacc[db] = mfma32(vf, pb[kc], oacc[db]);
-              oacc[db] = mfma32(vf, pl, oacc[db]);
-            }
-          }
-        }
+        for (int kbi = 0; kbi < NKB; ++kbi) s[kbi] = mfma32(kf[c & 1][kbi], qf[c], s[kbi]);
       }
     }
-    if (slot & 1) {
-      // tile k+1 must have landed before slot 2k+2 reads it; the four loads
-      // of each of tiles k+2 .. k+PF may still be in flight (s_waitcnt
-      // immediate: expcnt and lgkmcnt at their maxima, vmcnt in the low four
-      // bits)
-      const int k = slot >> 1;
-      const int newer = (ntl - 1 < k + PF ? ntl - 1 : k + PF) - (k + 1);
-      if (PF >= 3 && newer >= 2) {
-        __builtin_amdgcn_s_waitcnt(0x0F78);
-      } else if (newer >= 1) {
-        __builtin_amdgcn_s_waitcnt(0x0F74);
-      } else {
-        __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Vector phase of tile t.  steady: a tile the wave computes whole (no key
+  // masked for any of its rows) and that is not the split tile, so no
+  // per-tile check is made; given as std::true_type / std::false_type or as
+  // a run-time bool.
+  auto vector_phase = [&](const int t, auto steady_c) {
+    bool steady;
+    if constexpr (std::is_same_v<decltype(steady_c), bool>) {
+      steady = steady_c;
+    } else {
+      steady = decltype(steady_c)::value;
+    }
+    const int k0 = (t_first + t) * BN;
+    bool partial = false;
+    if (!steady)
+      partial = __builtin_amdgcn_readfirstlane((int)((k0 + BN > skv) || (CAUSAL && (k0 + BN - 1 > qw0 + off)) ||
+                                                     (W > 0 && k0 < qw0 + 31 + off - W + 1))) != 0;
+    if (partial) {
+#pragma unroll
+      for (int kbi = 0; kbi < NKB; ++kbi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {  // key = k0 + 32kbi + 8(r/4) + 4hh + r%4
+          const int kk = k0 + 32 * kbi + 8 * (r >> 2) + (r & 3);
+          if (kk >= lim_h || (LOCAL && kk < lo_h)) s[kbi][r] = -INFINITY;
+        }
+    }
+    // P~ against the current reference, S kept; this lane's share of the
+    // row sum as four independent chains
+    auto expo = [&]() {
+      float rp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const f32x16& sk = s[kc >> 1];
+        const int rb = 8 * (kc & 1);
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          e[j] = fast_exp2(fmaf(sk[rb + j], sl2, neg_ms));
+          rp[j & 3] += e[j];
+        }
+        pb[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       }
+      return (rp[0] + rp[1]) + (rp[2] + rp[3]);
+    };
+    float ps = expo();
+    // a share above 2^8 means some P~ above 2^8, and a row without a
+    // reference has no P~ yet: exact reference update, then P~ again
+    if (__any(ps > kSumCap || m_used == -INFINITY)) {
+      float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int kbi = 0; kbi < NKB; ++kbi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[kbi][r]);
+      const float mx = pair32_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+      const float m_new = fmaxf(m_used, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2((m_used - m_new) * sl2);
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_used = m_new;
+      neg_ms = (m_used == -INFINITY) ? 0.0f : -m_used * sl2;
+      ps = expo();
+    }
+    l_part += ps;
+    bool split = false;
+    if (!steady) split = __builtin_amdgcn_readfirstlane((int)precise(t)) != 0;
+    if (split) {
+      // the split P~V product of this tile (V of tile t is in stage
+      // t % STAGES); the fp32 P~ is recomputed with expo()'s
+      // instructions, so its bf16 part is pb exactly
+      const unsigned char* vb = smem + (t % STAGES) * STAGE_B + v_lane;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const f32x16& sk = s[kc >> 1];
+        const int rb = 8 * (kc & 1);
+        float lo[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) lo[j] = fast_exp2(fmaf(sk[rb + j], sl2, neg_ms)) - (float)pb[kc][j];
+        const bf16x8 pl = to_bf16x8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const unsigned char* a = vb + (NDB * kc + db) * 1024;
+          const bf16x8 vf = join_tr(lds_read_tr16(a), lds_read_tr16(a + 512));
+          oacc[db] = mfma32(vf, pb[kc], oacc[db]);
+          oacc[db] = mfma32(vf, pl, oacc[db]);
+        }
+      }
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) pb[kc] = bf16x8{};
+    }
+  };
+  // end of slot 2k+1: tile k+1 must have landed before slot 2k+2 reads it;
+  // the four loads of each of tiles k+2 .. k+PF may still be in flight
+  // (s_waitcnt immediate: expcnt and lgkmcnt at their maxima, vmcnt in the
+  // low four bits)
+  auto wait_tile = [&](const int k) {
+    const int newer = (ntl - 1 < k + PF ? ntl - 1 : k + PF) - (k + 1);
+    if (PF >= 3 && newer >= 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F78);
+    } else if (newer >= 1) {
+      __builtin_amdgcn_s_waitcnt(0x0F74);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+  };
+
+  // The tiles [st_lo, st_hi) (relative) are steady for this wave: computed,
+  // with no key masked for any of its rows (before the causal diagonal of
+  // its first row, after the window's lower edge for its last row, inside
+  // the keys), and not the split tile.  Masks are monotone in the tile
+  // index, so the steady tiles form one range.
+  auto fdiv = [](const int a, const int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); };
+  int st_lo = w_first - t_first;
+  int st_hi = nw - t_first;
+  st_hi = st_hi < skv / BN - t_first ? st_hi : skv / BN - t_first;                  // key tail
+  if (CAUSAL) {
+    const int d = fdiv(qw0 + off + 1, BN) - t_first;                                // diagonal
+    st_hi = st_hi < d ? st_hi : d;
+  }
+  if (W > 0) {
+    const int e = -fdiv(-(qw0 + off + 32 - W), BN) - t_first;                       // window edge
+    st_lo = st_lo > e ? st_lo : e;
+  }
+  if (few_keys && t_first == 0) st_lo = st_lo > 1 ? st_lo : 1;                      // split tile
+  st_lo = __builtin_amdgcn_readfirstlane(st_lo);
+  st_hi = __builtin_amdgcn_readfirstlane(st_hi);
+  // the vector phase of tile t, or P~ = 0 for a tile this wave does not
+  // compute (the next matrix phase then adds nothing for it)
+  auto vector_or_zero = [&](const int t) {
+    if constexpr (D == 64 || LOCAL) {
+      // one copy of the vector phase for both kinds of tile (two copies
+      // spill in these instantiations)
+      const bool steady = t >= st_lo && t < st_hi;
+      bool comp = steady;
+      if (!steady) comp = __builtin_amdgcn_readfirstlane((int)computes(t)) != 0;
+      if (comp) {
+        vector_phase(t, steady);
+      } else {
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) pb[kc] = bf16x8{};
+      }
+    } else {
+      if (__builtin_amdgcn_readfirstlane((int)computes(t)) != 0) {
+        vector_phase(t, std::false_type{});
+      } else {
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) pb[kc] = bf16x8{};
+      }
+    }
+  };
+  auto pv_last = [&](const int t) { return computes(t) && !precise(t); };
+  // Slots 0 .. 2 ntl + 1, one barrier each.  Group A: matrix phase of tile t
+  // in slot 2t, vector phase in slot 2t+1; group B one slot behind.  Tile
+  // u = k + PF is fetched into the stage of tile k + PF - STAGES, whose last
+  // read (its V, by group B) was in slot 2k-1: its V blocks by group B in
+  // slot 2k, its K blocks by group A in slot 2k+1, in both cases at the
+  // start of the loading group's vector phase.  (Loads issued by a wave that
+  // is about to run its matrix phase delay that phase's MFMAs, and a burst
+  // from all eight waves at once delays both phases: measured.)  Each group
+  // runs its own copy of the slot sequence.
+  //
+  // one slot pair of each group; steady: a tile of [st_lo, st_hi), where the
+  // vector phase makes no per-tile check
+  auto pair_a = [&](const int t, auto steady_c) {
+    if (t + PF < ntl) load_tile(t + PF);
+    if constexpr (decltype(steady_c)::value) {
+      vector_phase(t, std::true_type{});
+    } else {
+      vector_or_zero(t);
+    }
+    wait_tile(t);
+    __syncthreads();
+    matrix_steady(t + 1);
+    __syncthreads();
+  };
+  auto pair_b = [&](const int t, auto steady_c) {
+    matrix_steady(t);
+    wait_tile(t);
+    __syncthreads();
+    if (t + 1 + PF < ntl) load_tile(t + 1 + PF);
+    if constexpr (decltype(steady_c)::value) {
+      vector_phase(t, std::true_type{});
+    } else {
+      vector_or_zero(t);
     }
     __syncthreads();
+  };
+  if constexpr (D == 64 || LOCAL) {
+    // one loop per group; the steady test is made per tile (split loops
+    // spill registers in these instantiations)
+    if (__builtin_amdgcn_readfirstlane(grp) == 0) {
+      matrix_edge(0, false, computes(0));
+      __syncthreads();
+      for (int t = 0; t + 1 < ntl; ++t) {
+        if (t + PF < ntl) load_tile(t + PF);
+        vector_or_zero(t);
+        wait_tile(t);
+        __syncthreads();
+        matrix_steady(t + 1);
+        __syncthreads();
+      }
+      if (ntl > 0) {
+        vector_or_zero(ntl - 1);
+        wait_tile(ntl - 1);
+        __syncthreads();
+        matrix_edge(ntl, pv_last(ntl - 1), false);
+        __syncthreads();
+      }
+      __syncthreads();
+    } else {
+      if (PF < ntl) load_tile(PF);
+      __syncthreads();
+      if (ntl > 0) {
+        matrix_edge(0, false, computes(0));
+        wait_tile(0);
+        __syncthreads();
+        if (1 + PF < ntl) load_tile(1 + PF);
+        vector_or_zero(0);
+        __syncthreads();
+        for (int t = 1; t < ntl; ++t) {
+          matrix_steady(t);
+          wait_tile(t);
+          __syncthreads();
+          if (t + 1 + PF < ntl) load_tile(t + 1 + PF);
+          vector_or_zero(t);
+          __syncthreads();
+        }
+      }
+      matrix_edge(ntl, ntl > 0 && pv_last(ntl - 1), false);
+      __syncthreads();
+    }
+  } else {
+    if (__builtin_amdgcn_readfirstlane(grp) == 0) {
+      matrix_edge(0, false, computes(0));
+      __syncthreads();
+      // t in [0, ntl - 1): before, inside and after the steady range
+      const int e = ntl - 1;
+      const int a = st_lo < 0 ? 0 : (st_lo > e ? (e > 0 ? e : 0) : st_lo);
+      const int b = st_hi < a ? a : (st_hi > e ? (e > a ? e : a) : st_hi);
+      int t = 0;
+      for (; t < a; ++t) pair_a(t, std::false_type{});
+      for (; t < b; ++t) pair_a(t, std::true_type{});
+      for (; t < e; ++t) pair_a(t, std::false_type{});
+      if (ntl > 0) {
+        vector_or_zero(ntl - 1);
+        wait_tile(ntl - 1);
+        __syncthreads();
+        matrix_edge(ntl, pv_last(ntl - 1), false);
+        __syncthreads();
+      }
+      __syncthreads();
+    } else {
+      if (PF < ntl) load_tile(PF);
+      __syncthreads();
+      if (ntl > 0) {
+        matrix_edge(0, false, computes(0));
+        wait_tile(0);
+        __syncthreads();
+        if (1 + PF < ntl) load_tile(1 + PF);
+        vector_or_zero(0);
+        __syncthreads();
+        // t in [1, ntl)
+        const int a = st_lo < 1 ? 1 : (st_lo > ntl ? ntl : st_lo);
+        const int b = st_hi < a ? a : (st_hi > ntl ? ntl : st_hi);
+        int t = 1;
+        for (; t < a; ++t) pair_b(t, std::false_type{});
+        for (; t < b; ++t) pair_b(t, std::true_type{});
+        for (; t < ntl; ++t) pair_b(t, std::false_type{});
+      }
+      matrix_edge(ntl, ntl > 0 && pv_last(ntl - 1), false);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: O = acc / l (0 for rows that saw no key), LSE natural
