@@ -64,6 +64,9 @@
 //   * Attention sink (tutorial sections 4.6 and 4.7): in the epilogue the
 //     sink's exp2(sink log2(e) - m*) joins the denominator, with
 //     m* = max(m scale', sink log2(e)) so that a large sink cannot overflow.
+//   * The epilogue writes the normalised O tile into the (then idle) LDS
+//     ring and stores it as whole rows (tutorial section 3.4 (5): the MFMA
+//     fragment layout needs a staging hop for coalesced stores).
 #include <type_traits>
 
 #include "attn_common.h"
@@ -78,6 +81,14 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 // sequences a varlen call may have for the persistent (listed) order
 constexpr int kMaxListedSeqs = 1024;
+
+// one varlen item of the persistent order, as passed between waves through
+// LDS (state 0: an item, 1: padding, 2: the rounds are over)
+struct ListedItem {
+  int64_t q0, kv0, lse0;
+  int tile, len, state;
+  float sink;
+};
 
 #ifndef ATTN_PP_PRIO
 #define ATTN_PP_PRIO 2
@@ -117,6 +128,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE_B];
   __shared__ int seq_tiles[kMaxListedSeqs];  // varlen persistent order: query tiles per sequence
+  __shared__ ListedItem item_tab[NW];         // varlen persistent order: the items of NW rounds
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -440,10 +452,18 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
       }
       return (rp[0] + rp[1]) + (rp[2] + rp[3]);
     };
-    float ps = expo();
-    // a share above 2^8 means some P~ above 2^8, and a row without a
-    // reference has no P~ yet: exact reference update, then P~ again
-    if (__any(ps > kSumCap || m_used == -INFINITY)) {
+    // A share above 2^8 means some P~ above 2^8, and a row without a
+    // reference has no P~ yet: then the exact reference update, and P~
+    // again.  At d = 64 a wave whose rows have no reference yet (its first
+    // tile) goes to the update directly instead of discarding a first P~
+    // (2 % there; at d = 128 the extra branch costs registers and 2-10 %).
+    float ps = 0.0f;
+    bool exact = __any(m_used == -INFINITY);
+    if (D == 128 || !exact) {
+      ps = expo();
+      exact = __any(ps > kSumCap || m_used == -INFINITY);
+    }
+    if (exact) {
       float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int kbi = 0; kbi < NKB; ++kbi)
@@ -684,16 +704,14 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     l = l * o_mul + fast_exp2(sink_l2 - ms);
     ref_l2 = ms;
   }
-  // Dense tiles: O goes through LDS (the ring is free once the last slot's
-  // barrier has passed, and the next item's first loads come after the
-  // barrier that ends this item) so that the stores to HBM are whole rows:
-  // a lane holds 4-value pieces of one row, so a direct store instruction
-  // writes 16 bytes in each of 32 rows; from LDS it writes 1 KB of
-  // consecutive rows.  Rows are padded by 16 bytes, which spreads the 32
-  // rows of a write over the banks (two ways) and keeps every offset within
-  // a row an immediate.  Packed sequences store each lane's pieces directly
-  // (the staged form measured 6 % slower on the varlen workload).
-  if constexpr (!VARLEN) {
+  // O goes through LDS (the ring is free once the last slot's barrier has
+  // passed, and the next item's first loads come after the barrier that
+  // ends this item) so that the stores to HBM are whole rows: a lane holds
+  // 4-value pieces of one row, so a direct store instruction writes 16 bytes
+  // in each of 32 rows; from LDS it writes 1 KB of consecutive rows.  Rows
+  // are padded by 16 bytes, which spreads the 32 rows of a write over the
+  // banks (two ways) and keeps every offset within a row an immediate.
+  {
     constexpr int PROW = ROWB + 16;  // padded row
     static_assert(BM * PROW <= STAGES * STAGE_B, "the output tile fits the ring");
     const float inv = (qrow < sq && l > 0.0f) ? o_mul / l : 0.0f;
@@ -720,20 +738,6 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
       const u32x4 val = *(const u32x4*)(smem + row * PROW + 16 * c);
       if (q0 + row < sq) *(u32x4*)(O + (int64_t)(q0 + row) * q_rs + 8 * c) = val;
     }
-  } else if (qrow < sq) {
-    const float inv = l > 0.0f ? o_mul / l : 0.0f;
-    __bf16* orow = O + (int64_t)qrow * q_rs;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        bf16x4 w;
-        w[0] = (__bf16)(oacc[db][4 * rg + 0] * inv);
-        w[1] = (__bf16)(oacc[db][4 * rg + 1] * inv);
-        w[2] = (__bf16)(oacc[db][4 * rg + 2] * inv);
-        w[3] = (__bf16)(oacc[db][4 * rg + 3] * inv);
-        *(bf16x4*)(orow + 32 * db + 8 * rg + 4 * hh) = w;
-      }
   }
   if (qrow < sq && p.lse != nullptr && hh == 0)
     p.lse[lse_row + qrow] = l > 0.0f ? (ref_l2 + fast_log2(l)) * kLn2 : -INFINITY;
@@ -865,8 +869,9 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
   // heavy causal tile is paired with a light one.  Workgroup g sits on XCD
   // g % 8 and walks that XCD's share of the items.  Dense: the host makes the
   // item count a multiple of the grid.  Varlen: the listed order above; each
-  // item is located by a scan over the sequence lengths (the host enables
-  // this only when that scan is short and H is a multiple of 8).
+  // item is located by a search over the sequences' tile counts (the host
+  // enables this only when that search is short and H is a multiple of 8),
+  // NW rounds at a time.
   auto item = [&](const int r, bool& skip) {
     skip = false;
     if (p.persist_c == 0) {
@@ -885,12 +890,38 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
       if (v < 0) return false;
       dense_at(v);
     } else {
-      const int64_t f = persist_listed_index(blockIdx.x, r, p.persist_c, v_items);
-      if (f == -1) return false;
-      if (f < 0) {
+      // NW rounds at a time: wave w locates round r + w (the search is a
+      // chain of dependent LDS reads and cross-lane sums, so one wave per
+      // round takes it off the critical path), and each round reads its
+      // entry back
+      if (r % NW == 0) {
+        const int64_t f = persist_listed_index(blockIdx.x, r + wave, p.persist_c, v_items);
+        ListedItem e;
+        e.state = f == -1 ? 2 : (f < 0 ? 1 : 0);
+        if (f >= 0) {
+          listed_at(f, blockIdx.x % 8);
+          e.tile = a_tile;
+          e.len = a_sq;
+          e.q0 = a_q0;
+          e.kv0 = a_kv0;
+          e.lse0 = a_lse0;
+          e.sink = a_sink;
+        }
+        if (lane == 0) item_tab[wave] = e;
+        __syncthreads();
+      }
+      const ListedItem e = item_tab[r % NW];
+      if (e.state == 2) return false;
+      if (e.state == 1) {
         skip = true;
       } else {
-        listed_at(f, blockIdx.x % 8);
+        a_tile = e.tile;
+        a_sq = a_skv = e.len;
+        a_off = 0;
+        a_q0 = e.q0;
+        a_kv0 = e.kv0;
+        a_lse0 = e.lse0;
+        a_sink = e.sink;
       }
     }
     return true;
