@@ -42,6 +42,11 @@ P_ROUND = 2.0 ** -8      # bf16 relative rounding of P~
 FP32_SLACK = 2.0 ** -11  # every fp32 rounding together
 
 
+# every record of this session, for the parity tables at the end of the run
+RECORDS = []       # forward: check()
+GRAD_RECORDS = []  # backward: (check, gradient, max |error|, max |gradient|, relative L2 error)
+
+
 def say(msg):
     print(msg, flush=True)
     sys.stdout.flush()
@@ -128,5 +133,6 @@ def check(o, lse, o_ref, lse_ref, dtype, what="", a_ref=None, workload=False):
                 assert ratio[w] <= 1.0, (f"{what}: |dO| {err[w]:.3g} at {tuple(int(x) for x in w)} above the "
                                          f"rounding bound {tol[w]:.3g} (ref {o_ref[w]:.5g}, got {o[w]:.5g})")
     assert rec["max_dLSE"] <= LSE_BAR, f"{what}: max |dLSE| {rec['max_dLSE']:.3g}"
+    RECORDS.append(rec)
     say("PARITY " + json.dumps(rec))
     return rec

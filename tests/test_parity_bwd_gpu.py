@@ -23,7 +23,7 @@ import pytest
 from exact_attention_09_amd import synth
 from exact_attention_09_amd.workloads import WORKLOADS, host_f32, to_device
 from oracle import backward as bwd_oracle
-from parity import say
+from parity import GRAD_RECORDS, say
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +61,7 @@ def compare(got, want, what):
         rel2 = np.linalg.norm(g - w) / norm if norm > 0 else 0.0
         say(f"  {what}: {name} max|err| {err:.3g} of max|{name}| {scale:.3g} ({err / scale:.2e}), "
             f"rel L2 {rel2:.2e}")
+        GRAD_RECORDS.append((what, name, float(err), float(scale), float(rel2)))
         assert err <= REL * scale + 1e-4, f"{what}: {name} max|err| {err:.3g} > {REL} x {scale:.3g}"
         # (a gradient that is exactly zero, as with a single visible key, has
         # only the absolute floor above)
