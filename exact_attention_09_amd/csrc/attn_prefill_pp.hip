@@ -425,14 +425,31 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     if (!steady)
       partial = __builtin_amdgcn_readfirstlane((int)((k0 + BN > skv) || (CAUSAL && (k0 + BN - 1 > qw0 + off)) ||
                                                      (W > 0 && k0 < qw0 + 31 + off - W + 1))) != 0;
+    // 16-key chunk kc holds keys k0 + 16kc .. +15 (registers 8(kc%2) ..
+    // +7 of S block kc/2).  At d = 64 (128-key tiles), chunks from `live` on
+    // lie past the last key any row of this wave sees: they get no mask, no
+    // exponentials and P~ = 0 (a wave-uniform bound, so the tests on it are
+    // scalar branches; 8 % at d = 64, while at d = 128 the extra live
+    // ranges cost registers and up to 2 %, so there every chunk is live)
+    int live = NKC;
     if (partial) {
+      if constexpr (D == 64) {
+        int e = skv;
+        if (CAUSAL) e = e < qw0 + 32 + off ? e : qw0 + 32 + off;
+        const int n = (e - k0 + 15) >> 4;
+        live = __builtin_amdgcn_readfirstlane(n < 0 ? 0 : (n > NKC ? NKC : n));
+      }
 #pragma unroll
-      for (int kbi = 0; kbi < NKB; ++kbi)
+      for (int kc = 0; kc < NKC; ++kc) {
+        if (kc >= live) continue;
+        const int kbi = kc >> 1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {  // key = k0 + 32kbi + 8(r/4) + 4hh + r%4
+        for (int j = 0; j < 8; ++j) {  // key = k0 + 32kbi + 8(r/4) + 4hh + r%4
+          const int r = 8 * (kc & 1) + j;
           const int kk = k0 + 32 * kbi + 8 * (r >> 2) + (r & 3);
           if (kk >= lim_h || (LOCAL && kk < lo_h)) s[kbi][r] = -INFINITY;
         }
+      }
     }
     // P~ against the current reference, S kept; this lane's share of the
     // row sum as four independent chains
@@ -440,6 +457,10 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
       float rp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
+        if (kc >= live) {
+          pb[kc] = bf16x8{};
+          continue;
+        }
         const f32x16& sk = s[kc >> 1];
         const int rb = 8 * (kc & 1);
         float e[8];
@@ -466,9 +487,11 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     if (exact) {
       float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int kbi = 0; kbi < NKB; ++kbi)
+      for (int kc = 0; kc < NKC; ++kc) {
+        if (kc >= live) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[kbi][r]);
+        for (int j = 0; j < 8; ++j) mp[j & 3] = fmaxf(mp[j & 3], s[kc >> 1][8 * (kc & 1) + j]);
+      }
       const float mx = pair32_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
       const float m_new = fmaxf(m_used, mx);
       const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2((m_used - m_new) * sl2);
@@ -491,6 +514,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
       const unsigned char* vb = smem + (t % STAGES) * STAGE_B + v_lane;
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
+        if (kc >= live) continue;
         const f32x16& sk = s[kc >> 1];
         const int rb = 8 * (kc & 1);
         float lo[8];
