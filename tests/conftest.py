@@ -37,7 +37,8 @@ def pytest_terminal_summary(terminalreporter):
         tr.write_sep("-", f"backward parity: {len(grads)} gradients against the fp64 oracle")
         tr.write_line(f"{'check':58s} {'grad':4s} {'max|err|':>9s} {'max|grad|':>9s} {'ratio':>9s} {'rel L2':>9s}")
         for what, name, err, scale, rel2 in grads:
-            tr.write_line(f"{str(what)[:58]:58s} {name:4s} {err:9.2e} {scale:9.2e} {err / scale:9.2e} {rel2:9.2e}")
+            ratio = f"{err / scale:9.2e}" if scale >= 1e-6 else "        -"  # a gradient that is exactly 0
+            tr.write_line(f"{str(what)[:58]:58s} {name:4s} {err:9.2e} {scale:9.2e} {ratio} {rel2:9.2e}")
     if not recs:
         return
     tr.write_sep("-", f"parity: {len(recs)} checks against the fp64 oracle")
