@@ -303,13 +303,15 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     // the 16 P~V and 16 QK^T MFMAs are independent, so they are issued
     // alternately, each with its operand read a few MFMAs ahead
     {
-      if constexpr (LOCAL) {
+      if constexpr (LOCAL || BSHD || D == 64) {
         // The same order written out MFMA pair by MFMA pair, each operand
         // read AHEAD pairs earlier into a register ring, and fenced with
-        // sched_barrier.  In this instantiation the scheduler drops the
-        // sched_group_barrier pins below (every read then waited for
-        // lgkmcnt(0) before its MFMA: 23-29 % slower); where the pins hold,
-        // they are 0.5-1.5 % faster than this form.
+        // sched_barrier.  In these instantiations the scheduler drops the
+        // sched_group_barrier pins below in some or all matrix phases: every
+        // MFMA then takes its operand from the same four registers and
+        // waits for lgkmcnt(0) (window variant 23-29 % slower, BSHD 9-18 %).
+        // In the BHSD d = 128 instantiations the pins hold, and there they
+        // are about 1 % faster than this form.
         constexpr int AH = ATTN_PP_AHEAD;
         constexpr int R = AH + 1;
         bf16x8 vr[R], kr[R];
