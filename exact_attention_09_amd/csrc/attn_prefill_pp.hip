@@ -29,9 +29,11 @@
 //     holds P~ = 0 for it, so that tile's P~V adds nothing (K and V values
 //     are assumed finite, as the masked keys of a partial tile already
 //     require: 0 times a non-finite V would spread into the row).
-//   * Each wave keeps a single S tile in registers (32 rows x 64 keys), so the
-//     register footprint is that of the plain loop (2 waves per SIMD).
-//   * K/V tiles (64 keys) live in a ring of PF + 2 LDS stages of 32 KB.  A
+//   * Each wave keeps a single S tile in registers (32 rows x 64 keys; at
+//     d = 64, 128 keys), so the register footprint is that of the plain loop
+//     (2 waves per SIMD).
+//   * K/V tiles (64 keys; 128 at d = 64) live in a ring of PF + 2 LDS stages
+//     of 32 KB.  A
 //     tile is read during four consecutive slots (K by A then B, V by A then
 //     B two slots later).  Tiles go from HBM straight to LDS (buffer_load ...
 //     lds, no registers on the way), laid out in MFMA fragment order; tile u
@@ -44,9 +46,15 @@
 //     Each fragment read covers one contiguous block (1 KB or 512 B), so it
 //     is free of bank conflicts and its address is one register plus an
 //     immediate.
-//   * In steady state the P~V and QK^T MFMAs of a matrix phase (equal in
-//     number, d/8 each) are issued alternately, with their operand reads
-//     pinned a few MFMAs ahead.
+//   * In steady state the P~V and QK^T MFMAs of a matrix phase (16 each) are
+//     issued alternately, each with its operand read three MFMAs ahead:
+//     pinned with sched_group_barrier in the BHSD d = 128 instantiations,
+//     written out with a register ring and sched_barrier fences elsewhere
+//     (where the scheduler drops the pins and every MFMA would wait for its
+//     read).
+//   * At d = 64 the 16-key chunks of a diagonal tile past every row of the
+//     wave get no exponentials (P~ = 0), and a wave's first tile goes to the
+//     exact reference update directly.
 //   * Reference max without a per-tile max: P~ = exp2(S scale' - m scale')
 //     against the current reference m, S kept in registers.  If some lane's
 //     share of a row's tile sum exceeds 2^8 (so some P~ > 2^8), or a row has
@@ -67,6 +75,9 @@
 //   * The epilogue writes the normalised O tile into the (then idle) LDS
 //     ring and stores it as whole rows (tutorial section 3.4 (5): the MFMA
 //     fragment layout needs a staging hop for coalesced stores).
+//   * Work order: a persistent grid of one workgroup per CU where the items
+//     allow it, XCD-aware, pairing heavy and light causal tiles; packed
+//     sequences in a listed order located eight rounds at a time.
 #include <type_traits>
 
 #include "attn_common.h"
