@@ -127,6 +127,9 @@ EDGE = [
     ("bf16", 1, 2, 2, 300, 130, 64, True, 0),
     ("bf16", 1, 3, 3, 129, 1, 64, False, 0),        # one key
     ("bf16", 2, 6, 3, 200, 200, 64, True, 0),       # GQA group 2, d = 64
+    ("bf16", 2, 4, 2, 77, 300, 64, True, 0),        # d = 64, Sq < Skv causal, ragged key tail
+    ("bf16", 1, 2, 2, 257, 333, 64, False, 0),      # d = 64 non-causal, ragged tails in both
+    ("bf16", 1, 4, 4, 150, 150, 64, True, 0),       # d = 64 causal, diagonals inside 16-key chunks
     ("bf16", 1, 4, 4, 128, 0, 128, False, 0),       # no keys at all
     ("bf16", 1, 2, 1, 1, 1000, 128, False, 0),      # decode, heuristic split
     ("bf16", 2, 8, 2, 1, 333, 64, True, 3),         # decode d = 64 (causal is moot at Sq = 1)
