@@ -627,11 +627,22 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(const Params p) {
     }
     wait_tile(t);
     __syncthreads();
-    matrix_steady(t + 1);
+    // packed sequences: outside the steady range, a wave with neither tile
+    // t nor t+1 to compute (past its rows' diagonal) skips the products
+    // (P~ = 0, S unused): no time inside the slot, but less power
+    if constexpr (decltype(steady_c)::value || !VARLEN) {
+      matrix_steady(t + 1);
+    } else if (__builtin_amdgcn_readfirstlane((int)(computes(t) || computes(t + 1))) != 0) {
+      matrix_steady(t + 1);
+    }
     __syncthreads();
   };
   auto pair_b = [&](const int t, auto steady_c) {
-    matrix_steady(t);
+    if constexpr (decltype(steady_c)::value || !VARLEN) {
+      matrix_steady(t);
+    } else if (__builtin_amdgcn_readfirstlane((int)(computes(t - 1) || computes(t))) != 0) {
+      matrix_steady(t);
+    }
     wait_tile(t);
     __syncthreads();
     if (t + 1 + PF < ntl) load_tile(t + 1 + PF);
