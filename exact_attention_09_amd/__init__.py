@@ -18,7 +18,8 @@ Names mirror the C entry points:
   varlen) tensors, plus the window and sinks;
 * ``attn_bwd`` computes dq, dk, dv from the forward's o and lse (dense or
   packed varlen), ``attn_bwd_window_sink`` the same for the window/sink
-  forward (plus the sink gradients);
+  forward (plus the sink gradients), ``attn_bwd_layout`` either of them in
+  the layouts of ``attn_fwd_layout``;
 * ``attn_fwd_paged`` runs split-KV decode over a paged KV cache (block
   table and per-sequence key counts) and returns ``(o, lse)``;
 * ``attn_workspace_bytes``, ``attn_decode_num_splits``,
@@ -41,7 +42,8 @@ ATTN_MAX_SPLITS = 256
 ATTN_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_noalloc", "attn_fwd_window_sink", "attn_fwd_layout",
-            "attn_fwd_paged", "attn_bwd", "attn_bwd_window_sink", "attn_bwd_workspace_bytes", "attn_workspace_bytes",
+            "attn_fwd_paged", "attn_bwd", "attn_bwd_window_sink", "attn_bwd_layout", "attn_bwd_workspace_bytes",
+            "attn_workspace_bytes",
             "attn_decode_num_splits", "attn_status_string", "attn_last_error")
 
 
@@ -98,6 +100,10 @@ def load_library(path: str = LIB_PATH):
     lib.attn_bwd_window_sink.restype = ctypes.c_int
     lib.attn_bwd_window_sink.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [
         ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(AttnOpts)]
+    lib.attn_bwd_layout.restype = ctypes.c_int
+    lib.attn_bwd_layout.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.POINTER(AttnOpts)]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 3
     lib.attn_workspace_bytes.restype = ctypes.c_size_t
@@ -455,6 +461,73 @@ def attn_bwd_window_sink(q, k, v, o, lse, dout, *, window: int = 0, sinks=None, 
                                   _ptr(dv), _ptr(dsinks) if sinks is not None else None, B, H, Hkv, Sq, Skv, d,
                                   float(scale), _ptr(cu_seqlens), int(window), _ptr(sinks), ctypes.c_void_p(stream),
                                   ctypes.byref(opts))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_last_error())
+    return dq, dk, dv, (dsinks if sinks is not None else None)
+
+
+def attn_bwd_layout(q, k, v, o, lse, dout, *, layout: str = "bshd", causal: bool = False, window: int = 0,
+                    sinks=None, scale: float | None = None, cu_seqlens=None, dq=None, dk=None, dv=None, dsinks=None,
+                    stream=None, workspace=None):
+    """Gradients through ``attn_bwd_layout``, the inverse of
+    ``attn_fwd_layout``: the same layouts and shapes (``layout="bshd"``: q,
+    o, dout [B,Sq,H,d], k, v [B,Skv,Hkv,d], packed [T,H,d] / [T,Hkv,d] with
+    ``cu_seqlens``; ``layout="bhsd"``: those of ``attn_bwd``), lse as the
+    forward wrote it, ``window``/``sinks`` as for ``attn_bwd_window_sink``
+    (need ``causal``).  Returns ``(dq, dk, dv, dsinks)`` (``dsinks`` None
+    without sinks)."""
+    import torch
+    lib = load_library()
+    lay = {"bhsd": ATTN_BHSD, "bshd": ATTN_BSHD}[layout]
+    if lay == ATTN_BSHD:
+        if cu_seqlens is not None:
+            if q.dim() != 3 or k.dim() != 3:
+                raise ValueError("packed varlen tensors are [T, H, d]")
+            T, H, d = q.shape
+            Tk, Hkv, dk_ = k.shape
+            if Tk != T:
+                raise ValueError("varlen q and k must hold the same tokens")
+            B, Sq, Skv = cu_seqlens.numel() - 1, T, T
+            lse_shape = (H, T)
+        else:
+            if q.dim() != 4 or k.dim() != 4:
+                raise ValueError("BSHD tensors are [B, S, H, d]")
+            B, Sq, H, d = q.shape
+            Bk, Skv, Hkv, dk_ = k.shape
+            if Bk != B:
+                raise ValueError("q and k batch sizes differ")
+            lse_shape = (B, H, Sq)
+    else:
+        B, H, Hkv, Sq, Skv, d, dk_ = _shapes(q, k, cu_seqlens)
+        lse_shape = tuple(q.shape[:-1])
+    if dk_ != d or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape) \
+            or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != tuple(lse_shape):
+        raise ValueError("shapes: o and dout as q, v as k, lse [B,H,Sq] ([H,T] varlen)")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor on the GPU")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 tensor on the GPU")
+    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_cuda or sinks.numel() != H
+                              or not sinks.is_contiguous()):
+        raise ValueError("sinks must be a contiguous float32 tensor of H values on the GPU")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise ValueError("cu_seqlens must be an int32 tensor on the GPU")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if sinks is not None and dsinks is None:
+        dsinks = torch.empty(H, dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    opts = AttnOpts(0, workspace.data_ptr() if workspace is not None else None,
+                    workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    st = lib.attn_bwd_layout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                             _ptr(dsinks) if sinks is not None else None, B, H, Hkv, Sq, Skv, d, float(scale),
+                             int(bool(causal)), _ptr(cu_seqlens), lay, int(window), _ptr(sinks),
+                             ctypes.c_void_p(stream), ctypes.byref(opts))
     if st != ATTN_OK:
         raise AttnError(st, attn_last_error())
     return dq, dk, dv, (dsinks if sinks is not None else None)

@@ -413,14 +413,15 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Sq) {
 
 namespace {
 
-// The backward behind attn_bwd and attn_bwd_window_sink: window > 0 and
-// sinks != NULL are causal (the caller validated that).
+// The backward behind attn_bwd, attn_bwd_window_sink and attn_bwd_layout:
+// window > 0 and sinks != NULL are causal (the callers validate that).
 attn_status backward(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                      void* dq, void* dk, void* dv, int B, int H, int Hkv, int Sq, int Skv, int d, float scale,
                      int causal, const int32_t* cu_seqlens, int window, const float* sinks, float* dsinks,
-                     void* stream, const attn_opts* opts) {
+                     void* stream, const attn_opts* opts, attn_layout layout) {
   g_err[0] = '\0';
   // ---- validation: no HIP call until every check has passed
+  if (layout != ATTN_BHSD && layout != ATTN_BSHD) return fail(ATTN_EINVAL, "unknown layout %d", (int)layout);
   if (window < 0) return fail(ATTN_EINVAL, "window must be >= 0 (got %d)", window);
   if (sinks != nullptr && (!aligned(sinks, 4) || dsinks == nullptr || !aligned(dsinks, 4)))
     return fail(ATTN_EINVAL, "sinks need a 4-byte aligned dsinks output of H floats");
@@ -447,6 +448,9 @@ attn_status backward(const void* q, const void* k, const void* v, const void* o,
   const long double q_elems = (long double)(varlen ? 1 : B) * H * Sq * d;
   const long double kv_elems = (long double)(varlen ? 1 : B) * Hkv * Skv * d;
   if (q_elems > 9.0e18L || kv_elems > 9.0e18L) return fail(ATTN_EINVAL, "tensor too large");
+  // a row of q (H d elements apart in BSHD) times the rows of one tile (at
+  // most 64) must stay inside the 32-bit byte range of a buffer descriptor
+  if ((long)H * d >= (1L << 23)) return fail(ATTN_EINVAL, "H * d too large (must be below 2^23)");
   const long q_tiles = varlen ? (long)H * (Sq / 128 + B) : (long)B * H * attn::ceil_div(Sq, 128);
   const long k_tiles = varlen ? (long)Hkv * (Skv / 128 + B) : (long)B * Hkv * attn::ceil_div(Skv, 128);
   if (q_tiles > 0x7ffffff0L || k_tiles > 0x7ffffff0L) return fail(ATTN_EINVAL, "too many tiles");
@@ -460,8 +464,9 @@ attn_status backward(const void* q, const void* k, const void* v, const void* o,
   p.sinks = sinks;
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-  p.q_rs = d;
-  p.kv_rs = d;
+  p.bshd = layout == ATTN_BSHD ? 1 : 0;
+  p.q_rs = p.bshd ? H * d : d;
+  p.kv_rs = p.bshd ? Hkv * d : d;
   hipStream_t st = (hipStream_t)stream;
 
   if (Sq == 0) {  // dense only: a varlen call with no token returned above
@@ -521,7 +526,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* dq, void* dk, void* dv, int B, int H, int Hkv, int Sq, int Skv, int d, float scale,
                      int causal, const int32_t* cu_seqlens, void* stream, const attn_opts* opts) {
   return backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Sq, Skv, d, scale, causal, cu_seqlens, 0, nullptr,
-                  nullptr, stream, opts);
+                  nullptr, stream, opts, ATTN_BHSD);
 }
 
 attn_status attn_bwd_window_sink(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -529,7 +534,19 @@ attn_status attn_bwd_window_sink(const void* q, const void* k, const void* v, co
                                  int Sq, int Skv, int d, float scale, const int32_t* cu_seqlens, int window,
                                  const float* sinks, void* stream, const attn_opts* opts) {
   return backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Sq, Skv, d, scale, 1, cu_seqlens, window, sinks,
-                  dsinks, stream, opts);
+                  dsinks, stream, opts, ATTN_BHSD);
+}
+
+attn_status attn_bwd_layout(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, float* dsinks, int B, int H, int Hkv,
+                            int Sq, int Skv, int d, float scale, int causal, const int32_t* cu_seqlens,
+                            attn_layout layout, int window, const float* sinks, void* stream,
+                            const attn_opts* opts) {
+  g_err[0] = '\0';
+  if ((window > 0 || sinks != nullptr) && !causal)
+    return fail(ATTN_EINVAL, "a window or sinks need causal attention");
+  return backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Sq, Skv, d, scale, causal, cu_seqlens, window, sinks,
+                  dsinks, stream, opts, layout);
 }
 
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,

@@ -45,19 +45,27 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 // Per row: Delta = rowsum(dO * O) in fp32, and the forward's LSE in log2
 // units for exp2, with +inf for a row that saw no key (LSE = -inf) so that
-// its P = exp2(s' - LSE') is 0.  D/8 lanes per row, 16 bytes each.
-template <int D>
+// its P = exp2(s' - LSE') is 0.  D/8 lanes per row, 16 bytes each.  Rows
+// are counted in the LSE's (batch, head, position) order; under BSHD row
+// (b, h, s) of O and dO sits at element ((b S + s) H + h) D (S rows per
+// head; packed sequences: b = 0, S = T).
+template <int D, bool BSHD>
 __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
                                                    const float* __restrict__ lse, float* __restrict__ delta,
-                                                   float* __restrict__ lse2, long rows) {
+                                                   float* __restrict__ lse2, long rows, int H, int S) {
   constexpr int TPR = D / 8;
   constexpr int RPB = 256 / TPR;
   const int sub = threadIdx.x % TPR;
   const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
   float acc = 0.0f;
   if (row < rows) {
-    const bf16x8 a = *(const bf16x8*)(o + row * D + 8 * sub);
-    const bf16x8 b = *(const bf16x8*)(dout + row * D + 8 * sub);
+    long el = row * D;
+    if constexpr (BSHD) {
+      const long bh = row / S, s = row - bh * S, b = bh / H, h = bh - b * H;
+      el = ((b * S + s) * H + h) * D;
+    }
+    const bf16x8 a = *(const bf16x8*)(o + el + 8 * sub);
+    const bf16x8 b = *(const bf16x8*)(dout + el + 8 * sub);
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc += (float)a[j] * (float)b[j];
   }
@@ -102,7 +110,8 @@ __global__ __launch_bounds__(256) void dsink_kernel(const float* __restrict__ si
 // run of 1 KB blocks; lane L of a block load writes bytes 16L .. 16L+15 of
 // the block, which is row L / (2D/16) of the block at chunk position
 // L % (2D/16), so the lane fetches the logical chunk that the swizzle puts
-// there.  `voff(j)` is that lane's byte offset in the HBM tile for block j.
+// there.  `voff(j, lane, rsb)` is that lane's byte offset in the HBM tile for
+// block j, with rows rsb bytes apart there (2D in BHSD, 2 H D in BSHD).
 template <int D, int ROWS>
 struct SwizzledTile {
   static constexpr int ROWB = 2 * D;
@@ -110,9 +119,9 @@ struct SwizzledTile {
   static constexpr int RPB = 1024 / ROWB;   // rows per 1 KB block
   static constexpr int NBLK = ROWS / RPB;   // blocks per tile
   static constexpr int BYTES = ROWS * ROWB;
-  __device__ static int voff(int j, int lane) {
+  __device__ static int voff(int j, int lane, int rsb) {
     const int r = j * RPB + lane / CPR;
-    return r * ROWB + (((lane % CPR) ^ swz<D>(r)) << 4);
+    return r * rsb + (((lane % CPR) ^ swz<D>(r)) << 4);
   }
 };
 
@@ -154,7 +163,10 @@ __device__ inline bf16x8 half_bf16(const f32x16& a, int h) {
 // vector work differs.  (A one-wave-per-32-keys kernel holding both
 // accumulators needs about 400 registers, so only one wave fits a SIMD; even
 // written out as a software pipeline it ran 2-4 % slower than this pair.)
-template <int D, bool CAUSAL, bool VARLEN, bool LOCAL>
+// BSHD: q, dO [B, Sq, H, d] and k, v, dK, dV [B, Skv, Hkv, d] (packed
+// sequences: [T, H, d], [T, Hkv, d]); rows H d (Hkv d) elements apart, known
+// at run time; off, every stride is the compile-time d.
+template <int D, bool CAUSAL, bool VARLEN, bool LOCAL, bool BSHD>
 __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const __bf16* __restrict__ dout,
                                                            const float* __restrict__ delta,
                                                            const float* __restrict__ lse2, __bf16* __restrict__ dk,
@@ -226,13 +238,17 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
   const int k0 = kt * BK;
   const int kw0 = k0 + 32 * kb;
   const int krow = kw0 + l32;
+  // element offset of this sequence's key row 0 and the row strides
+  const int q_rs = BSHD ? __builtin_amdgcn_readfirstlane(p.q_rs) : D;
+  const int kv_rs = BSHD ? __builtin_amdgcn_readfirstlane(p.kv_rs) : D;
+  const int64_t kv_el = BSHD ? (((int64_t)b * p.Skv + q_row_shift) * p.Hkv + kvh) * D : kv_row0 * D;
 
   // this lane's K row (S side) or V row (dP side): the B operand
-  const __bf16* __restrict__ KV = (const __bf16*)(s_side ? p.k : p.v) + kv_row0 * D;
+  const __bf16* __restrict__ KV = (const __bf16*)(s_side ? p.k : p.v) + kv_el;
   bf16x8 kvf[NDC];
 #pragma unroll
   for (int c = 0; c < NDC; ++c)
-    kvf[c] = krow < skv ? *(const bf16x8*)(KV + (int64_t)krow * D + 16 * c + 8 * hh) : bf16x8{};
+    kvf[c] = krow < skv ? *(const bf16x8*)(KV + (int64_t)krow * kv_rs + 16 * c + 8 * hh) : bf16x8{};
 
   f32x16 acc[NDB];  // dV^T (S side) or dK^T (dP side): rows d, column = this lane's key
 #pragma unroll
@@ -258,7 +274,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
 
   int voff[BPW];
 #pragma unroll
-  for (int i = 0; i < BPW; ++i) voff[i] = Tile::voff(kb * BPW + i, lane);
+  for (int i = 0; i < BPW; ++i) voff[i] = Tile::voff(kb * BPW + i, lane, 2 * q_rs);
   float lse_reg = 0.0f, del_reg = 0.0f;
   auto step_src = [&](int s, int& h, int& q0) {
     h = kvh * p.group + s / per_head;
@@ -274,8 +290,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
       del_reg = i < sq ? delta[row0 + lane] : 0.0f;
     }
     const int nrows = sq - q0 < BQ ? sq - q0 : BQ;
-    const __bf16* src = s_side ? (const __bf16*)p.q + row0 * D : dout + row0 * D;
-    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(src, nrows * 2 * D);
+    // the tile's first row in q (dO); the descriptor ends right after row
+    // nrows-1, so rows past it read as zeros
+    const int64_t q_el = BSHD ? (((int64_t)b * p.Sq + q_row_shift + q0) * p.H + h) * D : row0 * D;
+    const __bf16* src = s_side ? (const __bf16*)p.q + q_el : dout + q_el;
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(src, (nrows - 1) * 2 * q_rs + 2 * D);
     const unsigned dst = lds_u32(smem) + (s & 1) * STAGE + (s_side ? 0 : TILE) + kb * BPW * 1024;
 #pragma unroll
     for (int i = 0; i < BPW; ++i) load_lds16(rs, voff[i], 0, dst + i * 1024);
@@ -445,7 +464,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
 
   // dV = dV^T^T (S side), dK = s dK^T^T (dP side): this lane's key row
   if (krow < skv) {
-    __bf16* row = (s_side ? dv : dk) + (kv_row0 + krow) * D;
+    __bf16* row = (s_side ? dv : dk) + kv_el + (int64_t)krow * kv_rs;
     const float sc = s_side ? 1.0f : p.scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -464,8 +483,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
 // Queries stationary: workgroup (b, query head, 128 queries), wave w owns
 // queries q0 + 32w .. +31 (one per lane of a half-wave pair); key tiles of 64
 // rows stream through LDS, double buffered, each worked in two 32-key
-// halves.  Two workgroups share a CU.
-template <int D, bool CAUSAL, bool VARLEN, bool LOCAL>
+// halves.  Two workgroups share a CU.  BSHD as for the dK/dV kernel.
+template <int D, bool CAUSAL, bool VARLEN, bool LOCAL, bool BSHD>
 __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16* __restrict__ dout,
                                                     const float* __restrict__ delta, const float* __restrict__ lse2,
                                                     __bf16* __restrict__ dq) {
@@ -493,7 +512,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
   // K/V stream in one L2); varlen: (query head, tile of the packed
   // sequences), located through cu_seqlens.
   int tile, sq, skv;
-  int64_t row0, kv0;  // this head's (sequence's) query row 0 and key row 0
+  int64_t row0, kv0;    // this head's (sequence's) query row 0 and key row 0, in rows of d
+  int64_t q_el, kv_el;  // the element offsets of those rows in q (dO, dQ) and k (v)
   if constexpr (VARLEN) {
     const int qtu = p.tiles_per_head;
     int h, s0, len;
@@ -510,6 +530,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
     sq = skv = len;
     row0 = (int64_t)h * p.Sq + s0;
     kv0 = (int64_t)(h / p.group) * p.Sq + s0;
+    q_el = BSHD ? ((int64_t)s0 * p.H + h) * D : row0 * D;
+    kv_el = BSHD ? ((int64_t)s0 * p.Hkv + h / p.group) * D : kv0 * D;
   } else {
     const int qtiles = ceil_div(p.Sq, BMQ);
     const int nbh = p.B * p.H;
@@ -523,24 +545,28 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
     skv = p.Skv;
     row0 = (int64_t)bh * sq;
     kv0 = ((int64_t)b * p.Hkv + h / p.group) * skv;
+    q_el = BSHD ? ((int64_t)b * sq * p.H + h) * D : row0 * D;
+    kv_el = BSHD ? ((int64_t)b * skv * p.Hkv + h / p.group) * D : kv0 * D;
   }
   const int off = skv - sq;
   const int q0 = tile * BMQ;
   const int qw0 = q0 + 32 * wave;
   const int qrow = qw0 + l32;
 
-  const __bf16* __restrict__ Q = (const __bf16*)p.q + row0 * D;
-  const __bf16* __restrict__ dO = dout + row0 * D;
-  const __bf16* __restrict__ K = (const __bf16*)p.k + kv0 * D;
-  const __bf16* __restrict__ V = (const __bf16*)p.v + kv0 * D;
+  const int q_rs = BSHD ? __builtin_amdgcn_readfirstlane(p.q_rs) : D;
+  const int kv_rs = BSHD ? __builtin_amdgcn_readfirstlane(p.kv_rs) : D;
+  const __bf16* __restrict__ Q = (const __bf16*)p.q + q_el;
+  const __bf16* __restrict__ dO = dout + q_el;
+  const __bf16* __restrict__ K = (const __bf16*)p.k + kv_el;
+  const __bf16* __restrict__ V = (const __bf16*)p.v + kv_el;
 
   bf16x8 qf[NDC], dof[NDC];
   float neg_lse = -INFINITY, del = 0.0f;  // -LSE log2(e) of this lane's row (-inf: P = 0)
   if (qrow < sq) {
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
-      qf[c] = *(const bf16x8*)(Q + (int64_t)qrow * D + 16 * c + 8 * hh);
-      dof[c] = *(const bf16x8*)(dO + (int64_t)qrow * D + 16 * c + 8 * hh);
+      qf[c] = *(const bf16x8*)(Q + (int64_t)qrow * q_rs + 16 * c + 8 * hh);
+      dof[c] = *(const bf16x8*)(dO + (int64_t)qrow * q_rs + 16 * c + 8 * hh);
     }
     neg_lse = -lse2[row0 + qrow];
     del = delta[row0 + qrow];
@@ -574,11 +600,13 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
   const bool loads_v = wu >= 2;
   int voff[BPW];
 #pragma unroll
-  for (int i = 0; i < BPW; ++i) voff[i] = Tile::voff((wu & 1) * BPW + i, lane);
+  for (int i = 0; i < BPW; ++i) voff[i] = Tile::voff((wu & 1) * BPW + i, lane, 2 * kv_rs);
   auto gload = [&](int t) {
     const int kb0 = t * BN;
     const int nrows = skv - kb0 < BN ? skv - kb0 : BN;
-    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc((loads_v ? V : K) + (int64_t)kb0 * D, nrows * 2 * D);
+    // the descriptor ends right after row nrows-1: rows past it read as zeros
+    const __amdgpu_buffer_rsrc_t rs =
+        uniform_rsrc((loads_v ? V : K) + (int64_t)kb0 * kv_rs, (nrows - 1) * 2 * kv_rs + 2 * D);
     const unsigned dst = lds_u32(smem) + (t & 1) * 2 * TILE + (loads_v ? TILE : 0) + (wu & 1) * BPW * 1024;
 #pragma unroll
     for (int i = 0; i < BPW; ++i) load_lds16(rs, voff[i], 0, dst + i * 1024);
@@ -698,7 +726,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
   }
 
   if (qrow < sq) {
-    __bf16* dqr = dq + (row0 + qrow) * D;
+    __bf16* dqr = dq + q_el + (int64_t)qrow * q_rs;
     const float sc = p.scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -712,7 +740,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
   }
 }
 
-template <int D, bool VARLEN, bool LOCAL>
+template <int D, bool VARLEN, bool LOCAL, bool BSHD>
 hipError_t launch_tiles(const Params& p, const __bf16* dout, float* delta, float* lse2, __bf16* dq, __bf16* dk,
                         __bf16* dv, hipStream_t st) {
   // dense non-causal grids are padded to a multiple of 8 for the XCD
@@ -731,13 +759,13 @@ hipError_t launch_tiles(const Params& p, const __bf16* dout, float* delta, float
       if (!p.causal) g1 = pad8(g1);
     }
     if (LOCAL)
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, true, VARLEN, true>), dim3((unsigned)g1), dim3(512), 0, st, q, dout,
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, true, VARLEN, true, BSHD>), dim3((unsigned)g1), dim3(512), 0, st, q, dout,
                          delta, lse2, dk, dv);
     else if (p.causal)
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, true, VARLEN, false>), dim3((unsigned)g1), dim3(512), 0, st, q, dout,
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, true, VARLEN, false, BSHD>), dim3((unsigned)g1), dim3(512), 0, st, q, dout,
                          delta, lse2, dk, dv);
     else
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, false, VARLEN, false>), dim3((unsigned)g1), dim3(512), 0, st, q, dout,
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, false, VARLEN, false, BSHD>), dim3((unsigned)g1), dim3(512), 0, st, q, dout,
                          delta, lse2, dk, dv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -751,13 +779,13 @@ hipError_t launch_tiles(const Params& p, const __bf16* dout, float* delta, float
     if (!p.causal) g2 = pad8(g2);
   }
   if (LOCAL)
-    hipLaunchKernelGGL((dq_kernel<D, true, VARLEN, true>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta, lse2,
+    hipLaunchKernelGGL((dq_kernel<D, true, VARLEN, true, BSHD>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta, lse2,
                        dq);
   else if (p.causal)
-    hipLaunchKernelGGL((dq_kernel<D, true, VARLEN, false>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta,
+    hipLaunchKernelGGL((dq_kernel<D, true, VARLEN, false, BSHD>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta,
                        lse2, dq);
   else
-    hipLaunchKernelGGL((dq_kernel<D, false, VARLEN, false>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta,
+    hipLaunchKernelGGL((dq_kernel<D, false, VARLEN, false, BSHD>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta,
                        lse2, dq);
   return hipGetLastError();
 }
@@ -769,8 +797,12 @@ hipError_t launch_bwd_d(const Params& p, const __bf16* dout, float* delta, float
   const int nb = var ? 1 : p.B;
   const long rows = (long)nb * p.H * p.Sq;
   constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
-                     (const __bf16*)p.o, dout, p.lse, delta, lse2, rows);
+  if (p.bshd)
+    hipLaunchKernelGGL((delta_kernel<D, true>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
+                       (const __bf16*)p.o, dout, p.lse, delta, lse2, rows, p.H, p.Sq);
+  else
+    hipLaunchKernelGGL((delta_kernel<D, false>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
+                       (const __bf16*)p.o, dout, p.lse, delta, lse2, rows, p.H, p.Sq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.sinks != nullptr) {
@@ -780,11 +812,18 @@ hipError_t launch_bwd_d(const Params& p, const __bf16* dout, float* delta, float
     if (e != hipSuccess) return e;
   }
   const bool local = p.window > 0;
+  if (p.bshd) {
+    if (var)
+      return local ? launch_tiles<D, true, true, true>(p, dout, delta, lse2, dq, dk, dv, st)
+                   : launch_tiles<D, true, false, true>(p, dout, delta, lse2, dq, dk, dv, st);
+    return local ? launch_tiles<D, false, true, true>(p, dout, delta, lse2, dq, dk, dv, st)
+                 : launch_tiles<D, false, false, true>(p, dout, delta, lse2, dq, dk, dv, st);
+  }
   if (var)
-    return local ? launch_tiles<D, true, true>(p, dout, delta, lse2, dq, dk, dv, st)
-                 : launch_tiles<D, true, false>(p, dout, delta, lse2, dq, dk, dv, st);
-  return local ? launch_tiles<D, false, true>(p, dout, delta, lse2, dq, dk, dv, st)
-               : launch_tiles<D, false, false>(p, dout, delta, lse2, dq, dk, dv, st);
+    return local ? launch_tiles<D, true, true, false>(p, dout, delta, lse2, dq, dk, dv, st)
+                 : launch_tiles<D, true, false, false>(p, dout, delta, lse2, dq, dk, dv, st);
+  return local ? launch_tiles<D, false, true, false>(p, dout, delta, lse2, dq, dk, dv, st)
+               : launch_tiles<D, false, false, false>(p, dout, delta, lse2, dq, dk, dv, st);
 }
 
 }  // namespace

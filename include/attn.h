@@ -233,7 +233,8 @@ attn_status attn_fwd_paged(const void* q, const void* k_cache, const void* v_cac
                            const attn_opts* opts);
 
 /* Backward pass: gradients of attn_fwd's output with respect to q, k, v
- * (bf16, BHSD, causal or not, dense or packed variable-length sequences).
+ * (bf16, BHSD, causal or not, dense or packed variable-length sequences;
+ * attn_bwd_layout below takes the BSHD layouts as well).
  * The pages name the backward only as the tutorial's section 5.4 Ascend
  * example (dQ partial tiles added with bf16 atomics, with the resulting
  * error); this library computes the derivative of the forward's definition
@@ -277,6 +278,26 @@ attn_status attn_bwd_window_sink(const void* q, const void* k, const void* v, co
                                  const float* lse, void* dq, void* dk, void* dv, float* dsinks, int B, int H, int Hkv,
                                  int Sq, int Skv, int d, float scale, const int32_t* cu_seqlens, int window,
                                  const float* sinks, void* stream, const attn_opts* opts);
+
+/* The general backward entry point: attn_bwd's arguments plus the tensor
+ * layout, a sliding window and sinks (as for attn_bwd_window_sink; window > 0
+ * or sinks != NULL need causal != 0, else ATTN_EINVAL).  attn_bwd and
+ * attn_bwd_window_sink are this call with layout = ATTN_BHSD.  Under
+ * ATTN_BSHD the bf16 tensors are those of attn_fwd_layout:
+ *   q, o, dout, dq : [B, Sq, H, d]      k, v, dk, dv : [B, Skv, Hkv, d]
+ *   varlen (cu_seqlens != NULL, packed tokens): [T, H, d] and [T, Hkv, d]
+ * while lse stays [B, H, Sq] ([H, T] varlen), as attn_fwd_layout writes it.
+ * The gradients are the same numbers in either layout (the same arithmetic
+ * in the same order), and the Delta/LSE workspace is the same size.
+ * H * d must be below 2^23 (ATTN_EINVAL otherwise), as for the forward.
+ * dsinks: fp32 [H], required when sinks != NULL.  Validation, errors,
+ * workspace and ordering on `stream` as for attn_bwd; an unknown layout is
+ * ATTN_EINVAL. */
+attn_status attn_bwd_layout(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, float* dsinks, int B, int H, int Hkv,
+                            int Sq, int Skv, int d, float scale, int causal, const int32_t* cu_seqlens,
+                            attn_layout layout, int window, const float* sinks, void* stream,
+                            const attn_opts* opts);
 
 /* Bytes of workspace attn_bwd needs (0 for invalid sizes). */
 size_t attn_bwd_workspace_bytes(int B, int H, int Sq);

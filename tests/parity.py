@@ -136,3 +136,26 @@ def check(o, lse, o_ref, lse_ref, dtype, what="", a_ref=None, workload=False):
     RECORDS.append(rec)
     say("PARITY " + json.dumps(rec))
     return rec
+
+
+GRAD_REL = 1e-2  # the backward bar: 1e-2 of each gradient tensor's largest magnitude
+
+
+def compare_grads(got, want, what):
+    """Backward parity: every element of each gradient within GRAD_REL of the
+    exact tensor's largest magnitude (plus 1e-4 absolute, for a gradient that
+    is exactly zero: a single visible key makes dq and dk vanish and leaves
+    rounding residue), and a relative L2 error of at most GRAD_REL."""
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        assert np.all(np.isfinite(g)), f"{what}: non-finite {name}"
+        scale = max(np.abs(w).max(initial=0.0), 1e-30)
+        err = np.abs(g - w).max(initial=0.0)
+        # relative L2 error, the measure the pages report for their backward
+        # (TileLang tutorial, section 5.4: about 1 % for dQ with bf16 atomics)
+        norm = np.linalg.norm(w)
+        rel2 = np.linalg.norm(g - w) / norm if norm > 0 else 0.0
+        say(f"  {what}: {name} max|err| {err:.3g} of max|{name}| {scale:.3g} ({err / scale:.2e}), "
+            f"rel L2 {rel2:.2e}")
+        GRAD_RECORDS.append((what, name, float(err), float(scale), float(rel2)))
+        assert err <= GRAD_REL * scale + 1e-4, f"{what}: {name} max|err| {err:.3g} > {GRAD_REL} x {scale:.3g}"
+        assert scale < 1e-6 or rel2 <= GRAD_REL, f"{what}: {name} relative L2 error {rel2:.3g}"

@@ -255,3 +255,35 @@ def test_bwd_empty_and_workspace(lib):
     # Delta and the log2 LSE: 3200 bytes each, each rounded up to 256
     assert ea.attn_bwd_workspace_bytes(2, 4, 100) == 2 * 3328
     assert ea.attn_bwd_workspace_bytes(-1, 4, 100) == 0
+
+
+def bwd_layout_call(lib, *, q=P, k=P, v=P, o=P, do=P, lse=P, dq=Q2, dk=Q2, dv=Q2, ds=None, B=1, H=4, Hkv=2, Sq=8,
+                    Skv=8, d=128, scale=0.1, causal=1, cu=None, layout=ea.ATTN_BSHD, window=0, sinks=None,
+                    opts=None):
+    return lib.attn_bwd_layout(q, k, v, o, do, lse, dq, dk, dv, ds, B, H, Hkv, Sq, Skv, d, scale, causal, cu, layout,
+                               window, sinks, None, ctypes.byref(opts) if opts is not None else None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=2), ea.ATTN_EINVAL),                       # unknown layout
+    (dict(layout=-1), ea.ATTN_EINVAL),
+    (dict(window=4, causal=0), ea.ATTN_EINVAL),             # a window needs causal
+    (dict(sinks=P, ds=Q2, causal=0), ea.ATTN_EINVAL),       # sinks need causal
+    (dict(sinks=P, ds=None), ea.ATTN_EINVAL),               # sinks without dsinks
+    (dict(window=-1), ea.ATTN_EINVAL),
+    (dict(H=1 << 17, Hkv=1 << 17, d=128), ea.ATTN_EINVAL),  # H d at 2^24: a tile leaves the descriptor's range
+    (dict(q=None), ea.ATTN_EINVAL),
+    (dict(d=96), ea.ATTN_EUNSUPPORTED),
+    (dict(dk=ctypes.c_void_p(0x200008)), ea.ATTN_EINVAL),
+    (dict(cu=ctypes.c_void_p(0x400000), Sq=8, Skv=9), ea.ATTN_EINVAL),
+    (dict(opts=ea.AttnOpts(0, 0x500000, 16)), ea.ATTN_EINVAL),
+])
+def test_bwd_layout_rejects_before_any_hip_call(lib, kw, status):
+    assert bwd_layout_call(lib, **kw) == status
+    assert ea.attn_last_error() != ""
+
+
+def test_bwd_layout_empty_problem_is_a_no_op(lib):
+    for layout in (ea.ATTN_BHSD, ea.ATTN_BSHD):
+        assert bwd_layout_call(lib, B=0, layout=layout) == ea.ATTN_OK
+        assert bwd_layout_call(lib, Sq=0, Skv=0, layout=layout) == ea.ATTN_OK
