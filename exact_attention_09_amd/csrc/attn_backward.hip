@@ -28,6 +28,11 @@
 // 16-byte chunk swizzle of attn_common.h; the transposed operands are read
 // with ds_read_b64_tr_b16.  P and dS are rounded to bf16 (nearest even) for
 // the products that consume them; every accumulation is fp32.
+//
+// Layouts: BHSD (rows d elements apart) or, in separate BSHD template
+// variants, [B, S, H, d] tensors whose rows are H d (Hkv d) elements apart;
+// the per-row Delta and log2 LSE stay in the LSE's [B, H, S] order either
+// way, and the arithmetic and its order do not depend on the layout.
 #include "attn_common.h"
 #include "attn_internal.h"
 
