@@ -1,5 +1,6 @@
 /*
- * Exact attention forward (FlashAttention) for AMD Instinct MI355X (gfx950).
+ * Exact attention (FlashAttention) for AMD Instinct MI355X (gfx950): the
+ * forward pass (prefill and split-KV decode) and its backward pass.
  *
  * C ABI: plain pointers and sizes, no C++ types, no exceptions across the
  * boundary.  Every pointer argument except `stream` points to device memory
@@ -62,10 +63,11 @@
  *
  * Ownership: the caller owns every buffer and the stream; the library keeps
  * no pointer after the call returns.  The only memory the library allocates
- * is the split-KV workspace of the decode path when the caller passes none,
- * taken and released stream-ordered (hipMallocAsync / hipFreeAsync) on
- * `stream`; besides, its code object holds the static scratch array of
- * attn_fwd_noalloc (ATTN_NOALLOC_SCRATCH_BYTES per GPU).
+ * is a workspace the caller did not pass: the split-KV partials of the decode
+ * path, and the per-row Delta and LSE of the backward, taken and released
+ * stream-ordered (hipMallocAsync / hipFreeAsync) on `stream`; besides, its
+ * code object holds the static scratch array of attn_fwd_noalloc
+ * (ATTN_NOALLOC_SCRATCH_BYTES per GPU).
  *
  * `stream` is a hipStream_t; NULL means the default stream.
  */
