@@ -20,6 +20,8 @@ Names mirror the C entry points:
   packed varlen), ``attn_bwd_window_sink`` the same for the window/sink
   forward (plus the sink gradients), ``attn_bwd_layout`` either of them in
   the layouts of ``attn_fwd_layout``;
+* ``flash_attention`` is the forward and backward as one differentiable
+  torch op (``attn_fwd_layout`` forward, ``attn_bwd_layout`` gradients);
 * ``attn_fwd_paged`` runs split-KV decode over a paged KV cache (block
   table and per-sequence key counts) and returns ``(o, lse)``;
 * ``attn_workspace_bytes``, ``attn_decode_num_splits``,
@@ -551,3 +553,52 @@ def raw_call(name: str, *args):
     """Call a C entry point with already-marshalled arguments (used by the
     ABI tests to drive the validation paths with raw pointers)."""
     return getattr(load_library(), name)(*args)
+
+
+_FLASH_FN = None
+
+
+def _flash_function():
+    """The torch.autograd.Function behind ``flash_attention`` (built on first
+    use, so that importing the package does not import torch)."""
+    global _FLASH_FN
+    if _FLASH_FN is not None:
+        return _FLASH_FN
+    import torch
+
+    class FlashAttention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, sinks, causal, window, scale, cu_seqlens, layout):
+            o, lse = attn_fwd_layout(q, k, v, layout=layout, causal=causal, window=window, sinks=sinks, scale=scale,
+                                     cu_seqlens=cu_seqlens)
+            ctx.save_for_backward(q, k, v, o, lse, sinks, cu_seqlens)
+            ctx.args = (causal, window, scale, layout)
+            ctx.mark_non_differentiable(lse)
+            return o, lse
+
+        @staticmethod
+        def backward(ctx, do, _dlse):
+            q, k, v, o, lse, sinks, cu_seqlens = ctx.saved_tensors
+            causal, window, scale, layout = ctx.args
+            dq, dk, dv, ds = attn_bwd_layout(q, k, v, o, lse, do.to(torch.bfloat16).contiguous(), layout=layout,
+                                             causal=causal, window=window, sinks=sinks, scale=scale,
+                                             cu_seqlens=cu_seqlens)
+            if sinks is None or not ctx.needs_input_grad[3]:
+                ds = None
+            return dq, dk, dv, ds, None, None, None, None, None
+
+    _FLASH_FN = FlashAttention
+    return _FLASH_FN
+
+
+def flash_attention(q, k, v, *, causal: bool = False, window: int = 0, sinks=None, scale: float | None = None,
+                    cu_seqlens=None, layout: str = "bshd", return_lse: bool = False):
+    """Exact attention as a differentiable torch op: ``attn_fwd_layout`` in
+    the forward, ``attn_bwd_layout`` for the gradients of q, k, v (and of
+    ``sinks`` when it requires them).  Tensors and options as for
+    ``attn_fwd_layout`` (bf16 q, k, v on the GPU, contiguous; ``layout``
+    "bshd" [B,S,H,d] or "bhsd" [B,H,S,d]; packed [T,H,d] with ``cu_seqlens``).
+    Returns o, or ``(o, lse)`` with ``return_lse`` (lse carries no gradient).
+    """
+    o, lse = _flash_function().apply(q, k, v, sinks, bool(causal), int(window), scale, cu_seqlens, layout)
+    return (o, lse) if return_lse else o
