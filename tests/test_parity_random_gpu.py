@@ -154,3 +154,97 @@ def test_random_backward(c):
         err = np.abs(ds.cpu().numpy().astype(np.float64) - want_ds)
         say(f"  random {name_of(c)}: dsinks max|err| {err.max():.3g} (terms up to {mag.max():.3g})")
         assert np.all(err <= 1e-2 * mag + 1e-6), f"dsinks error {err.max():.3g}"
+
+
+# ---- fp32 forward (BHSD, no window or sinks: the fp32 path's scope), 1e-5 bar
+
+def draw_f32(rng):
+    d = 64 if rng.random() < 0.5 else 128
+    H = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([x for x in (1, 2, 4, 8) if H % x == 0]))
+    causal = bool(rng.random() < 0.5)
+    if rng.random() < 0.3:
+        lengths = tuple(int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 300, int(rng.integers(1, 5))))
+        if sum(lengths) == 0:
+            lengths = (int(rng.integers(1, 200)),) + lengths[1:]
+        return dict(d=d, H=H, Hkv=Hkv, causal=causal, lengths=lengths, B=len(lengths), Sq=sum(lengths),
+                    Skv=sum(lengths))
+    B = int(rng.integers(1, 3))
+    Sq = 1 if rng.random() < 0.25 else int(rng.integers(1, 300))
+    return dict(d=d, H=H, Hkv=Hkv, causal=causal, lengths=None, B=B, Sq=Sq, Skv=int(rng.integers(1, 400)))
+
+
+F32 = [draw_f32(_RNG) for _ in range(10)]
+
+
+def name_f32(c):
+    shape = f"seqs{'-'.join(map(str, c['lengths']))}" if c["lengths"] else f"B{c['B']}-{c['Sq']}x{c['Skv']}"
+    return f"f32_d{c['d']}_H{c['H']}/{c['Hkv']}_{shape}_{'causal' if c['causal'] else 'full'}"
+
+
+@pytest.mark.parametrize("c", F32, ids=name_f32)
+def test_random_forward_f32(c):
+    import exact_attention_09_amd as ea
+    say(f"random fp32 forward {name_f32(c)}")
+    seed = 10 * (F32.index(c) + 9000)
+    H, Hkv, d = c["H"], c["Hkv"], c["d"]
+    if c["lengths"]:
+        qs, ks = (1, H, c["Sq"], d), (1, Hkv, c["Sq"], d)
+        cu = np.concatenate([[0], np.cumsum(c["lengths"])]).astype(np.int32)
+    else:
+        qs, ks = (c["B"], H, c["Sq"], d), (c["B"], Hkv, c["Skv"], d)
+        cu = None
+    q, k, v = (synth.normal_tensor(seed + i, s, "f32") for i, s in enumerate((qs, ks, ks)))
+    cut = torch.from_numpy(cu).cuda() if cu is not None else None
+    o, lse = ea.attn_fwd_f32(*(to_device(x, "f32") for x in (q, k, v)), causal=c["causal"], cu_seqlens=cut)
+    torch.cuda.synchronize()
+    o_ref, lse_ref, _ = reference(q, k, v, 1.0 / math.sqrt(d), c["causal"], cu_seqlens=cu)
+    check(o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "f32", f"random {name_f32(c)}")
+
+
+# ---- paged split-KV decode: random page sizes, key counts and scattered pages
+
+def draw_paged(rng):
+    d = 64 if rng.random() < 0.4 else 128
+    H = int(rng.choice([1, 4, 8, 16]))
+    Hkv = int(rng.choice([x for x in (1, 2, 4, 8) if H % x == 0]))
+    page = int(rng.choice([16, 32, 64, 128, 256]))
+    B = int(rng.integers(1, 5))
+    max_pages = int(rng.integers(1, 12))
+    seqlens = [int(rng.integers(0, max_pages * page + 1)) for _ in range(B)]
+    splits = int(rng.choice([0, 1, 3, 16]))
+    return dict(d=d, H=H, Hkv=Hkv, page=page, B=B, max_pages=max_pages, seqlens=tuple(seqlens), splits=splits)
+
+
+PAGED = [draw_paged(_RNG) for _ in range(10)]
+
+
+def name_paged(c):
+    return (f"paged_d{c['d']}_H{c['H']}/{c['Hkv']}_p{c['page']}_x{c['max_pages']}_lens"
+            f"{'-'.join(map(str, c['seqlens']))}_s{c['splits']}")
+
+
+@pytest.mark.parametrize("c", PAGED, ids=name_paged)
+def test_random_paged_decode(c):
+    import exact_attention_09_amd as ea
+    from oracle import paged as paged_oracle
+    say(f"random paged decode {name_paged(c)}")
+    seed = 10 * (PAGED.index(c) + 9500)
+    rng = np.random.default_rng(seed)
+    B, H, Hkv, d, page, mp = c["B"], c["H"], c["Hkv"], c["d"], c["page"], c["max_pages"]
+    num_pages = B * mp + 3                                  # a few pages no sequence uses
+    table = rng.permutation(num_pages)[:B * mp].reshape(B, mp).astype(np.int32)
+    q = synth.normal_tensor(seed + 0, (B, H, 1, d), "bf16")
+    kc = synth.normal_tensor(seed + 1, (num_pages, Hkv, page, d), "bf16")
+    vc = synth.normal_tensor(seed + 2, (num_pages, Hkv, page, d), "bf16")
+    seqlens = np.asarray(c["seqlens"], np.int32)
+    o, lse = ea.attn_fwd_paged(to_device(q, "bf16"), to_device(kc, "bf16"), to_device(vc, "bf16"),
+                               torch.from_numpy(table).cuda(), torch.from_numpy(seqlens).cuda(),
+                               num_splits=c["splits"])
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(d)
+    q32, k32, v32 = (host_f32(x, "bf16") for x in (q, kc, vc))
+    o_ref, lse_ref = paged_oracle.paged_attention(q32[:, :, 0], k32, v32, table, seqlens, scale)
+    a_ref, _ = paged_oracle.paged_attention(q32[:, :, 0], k32, np.abs(v32), table, seqlens, scale)
+    check(o.float().cpu().numpy()[:, :, 0], lse.cpu().numpy(), o_ref, lse_ref, "bf16", f"random {name_paged(c)}",
+          a_ref=a_ref)
