@@ -52,6 +52,22 @@ def kernel_source_sha(workload: str = HEADLINE) -> str:
     return h.hexdigest()[:16]
 
 
+def provenance(wl) -> dict:
+    """What identifies this measurement without the repository's history:
+    the hashes of the kernel sources the profiles are keyed to, of the
+    library that ran, and the input recipe."""
+    from exact_attention_09_amd import synth
+    lib = os.path.join(ROOT, "exact_attention_09_amd", "libattn09.so")
+    h = hashlib.sha256()
+    with open(lib, "rb") as f:
+        for chunk in iter(lambda: f.read(1 << 20), b""):
+            h.update(chunk)
+    return {"kernel_source_sha16": {w: kernel_source_sha(w) for w in sorted(KERNEL_SOURCES)},
+            "library_sha16": h.hexdigest()[:16],
+            "inputs": (f"synth.normal_tensor, seed 1000 * {wl.wid} + tensor id (q {synth.TENSOR_Q}, k {synth.TENSOR_K}, "
+                       f"v {synth.TENSOR_V}), bf16 of N(0, 1)")}
+
+
 def read_traffic(workload: str):
     """HBM bytes per launch measured by rocprofv3 counters for the current
     kernel sources, or None when the summary is missing or stale."""
@@ -311,6 +327,7 @@ def main(argv=None):
                      "traffic": traffic, "kernel": "prefill_pp_kernel<128,false,false,false,false>",
                      "launch_ms_mean": round(t["event_ms_mean"], 4),
                      "frac_at_median": round(flops / (t["event_ms_median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "provenance": provenance(wl),
     }
     workloads = {}
     outputs = {}
