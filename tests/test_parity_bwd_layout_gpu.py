@@ -167,3 +167,23 @@ def test_bwd_thd_varlen(gpu, case):
                                                      1.0 / math.sqrt(d), causal)
                 compare_grads(tuple(g[:, :, sl] for g in grads), want[:3], f"THD {case} sequence {i}")
             s0 += n
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_bshd_workload_shape(gpu, causal):
+    """The 8K workload shape (B=1, H=32, S=8192, d=128) in BSHD: row strides
+    of 8 KB and offsets past 2^26 bytes, gradients bit for bit those of BHSD
+    (whose parity at this shape test_parity_bwd_gpu.py checks on a full
+    head)."""
+    ea = gpu
+    B, H, S, d = 1, 32, 8192, 128
+    say(f"backward BSHD at the workload shape, causal={causal}")
+    q, k, v, do = (to_device(synth.normal_tensor(4100 + 10 * int(causal) + i, (B, H, S, d), "bf16"), "bf16")
+                   for i in range(4))
+    o, lse = ea.attn_fwd_layout(q, k, v, layout="bhsd", causal=causal)
+    ref = ea.attn_bwd_layout(q, k, v, o, lse, do, layout="bhsd", causal=causal)
+    qb, kb, vb, dob, ob = (to_bshd(x) for x in (q, k, v, do, o))
+    got = ea.attn_bwd_layout(qb, kb, vb, ob, lse, dob, layout="bshd", causal=causal)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        assert_same(g, to_bshd(r), f"8K causal={causal} {name}")
