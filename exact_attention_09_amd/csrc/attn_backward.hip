@@ -9,16 +9,18 @@
 //   Delta_i = rowsum(dO_i * O_i)
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - Delta),  dQ = s dS K,  dK = s dS^T Q
 //
-// Three kernels, no atomics, fixed summation orders (bitwise reproducible):
-//   * delta_kernel: Delta in fp32;
+// Two tile kernels, no atomics, fixed summation orders (bitwise
+// reproducible), in this order:
+//   * dq_kernel: one workgroup per (batch, query head, 128 queries); each
+//     wave keeps its 32 queries' Q and dO rows in registers and walks the key
+//     tiles.  It also forms Delta (from the O rows) and the log2 LSE of its
+//     rows and leaves them in the workspace.  dQ costs a second computation
+//     of S and dP instead of atomic partial sums;
 //   * dkdv_pair_kernel: one workgroup per (batch, KV head, 128 keys); a pair
 //     of waves keeps 32 keys' K and V rows in registers (one each) and walks
 //     the query tiles of every query head of the group, so the grouped-query
-//     sum happens in registers;
-//   * dq_kernel: one workgroup per (batch, query head, 128 queries); each
-//     wave keeps its 32 queries' Q and dO rows in registers and walks the key
-//     tiles.  dQ costs a second computation of S and dP instead of atomic
-//     partial sums.
+//     sum happens in registers.  It reads Delta and the log2 LSE.
+// With sinks, dsink_kernel forms the sink gradients in between.
 //
 // Both tile kernels use v_mfma_f32_32x32x16_bf16 with the accumulator
 // arranged so that the exponentiated scores are directly the B operand of the
@@ -46,42 +48,7 @@ constexpr float kLog2e = 1.44269504088896340736f;
 #define ATTN_BWD_AHEAD_DQ 1
 #endif
 
-// ---------------------------------------------------------------- Delta
-
-// Per row: Delta = rowsum(dO * O) in fp32, and the forward's LSE in log2
-// units for exp2, with +inf for a row that saw no key (LSE = -inf) so that
-// its P = exp2(s' - LSE') is 0.  D/8 lanes per row, 16 bytes each.  Rows
-// are counted in the LSE's (batch, head, position) order; under BSHD row
-// (b, h, s) of O and dO sits at element ((b S + s) H + h) D (S rows per
-// head; packed sequences: b = 0, S = T).
-template <int D, bool BSHD>
-__global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                                                   const float* __restrict__ lse, float* __restrict__ delta,
-                                                   float* __restrict__ lse2, long rows, int H, int S) {
-  constexpr int TPR = D / 8;
-  constexpr int RPB = 256 / TPR;
-  const int sub = threadIdx.x % TPR;
-  const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
-  float acc = 0.0f;
-  if (row < rows) {
-    long el = row * D;
-    if constexpr (BSHD) {
-      const long bh = row / S, s = row - bh * S, b = bh / H, h = bh - b * H;
-      el = ((b * S + s) * H + h) * D;
-    }
-    const bf16x8 a = *(const bf16x8*)(o + el + 8 * sub);
-    const bf16x8 b = *(const bf16x8*)(dout + el + 8 * sub);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc += (float)a[j] * (float)b[j];
-  }
-#pragma unroll
-  for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && sub == 0) {
-    delta[row] = acc;
-    const float l = lse[row];
-    lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
-  }
-}
+// ---------------------------------------------------------------- sinks
 
 // dsink_h = -sum over the rows of head h of P_sink,i Delta_i, with
 // P_sink,i = exp(sink_h - LSE_i) (the forward's LSE counts the sink; a row
@@ -491,7 +458,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(const Params p, const
 // halves.  Two workgroups share a CU.  BSHD as for the dK/dV kernel.
 template <int D, bool CAUSAL, bool VARLEN, bool LOCAL, bool BSHD>
 __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16* __restrict__ dout,
-                                                    const float* __restrict__ delta, const float* __restrict__ lse2,
+                                                    float* __restrict__ delta, float* __restrict__ lse2,
                                                     __bf16* __restrict__ dq) {
   constexpr int BMQ = 128;
   constexpr int BN = 64;
@@ -573,8 +540,38 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
       qf[c] = *(const bf16x8*)(Q + (int64_t)qrow * q_rs + 16 * c + 8 * hh);
       dof[c] = *(const bf16x8*)(dO + (int64_t)qrow * q_rs + 16 * c + 8 * hh);
     }
-    neg_lse = -lse2[row0 + qrow];
-    del = delta[row0 + qrow];
+    // Delta = rowsum(dO * O) of this lane's row and the LSE in log2 units
+    // (+inf for a row that saw no key, so that its P is 0).  The sum runs in
+    // a fixed order: 8 products per 16-byte chunk, the chunks of this half
+    // of the row pairwise (a butterfly over the chunk index), then the other
+    // half from lane l ^ 32.  Both go to the workspace for the dK/dV and
+    // sink-gradient kernels, which run after this one.
+    const __bf16* __restrict__ orow = (const __bf16*)p.o + q_el + (int64_t)qrow * q_rs;
+    float part[NDC];
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) {
+      const bf16x8 a = *(const bf16x8*)(orow + 16 * c + 8 * hh);
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += (float)a[j] * (float)dof[c][j];
+      part[c] = acc;
+    }
+#pragma unroll
+    for (int m = NDC / 2; m >= 1; m >>= 1) {
+      float nxt[NDC];
+#pragma unroll
+      for (int c = 0; c < NDC; ++c) nxt[c] = part[c] + part[c ^ m];
+#pragma unroll
+      for (int c = 0; c < NDC; ++c) part[c] = nxt[c];
+    }
+    del = part[0] + __shfl_xor(part[0], 32, 64);
+    const float l = p.lse[row0 + qrow];
+    const float l2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    neg_lse = -l2;
+    if (hh == 0) {
+      delta[row0 + qrow] = del;
+      lse2[row0 + qrow] = l2;
+    }
   } else {
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
@@ -747,13 +744,39 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const Params p, const __bf16
 
 template <int D, bool VARLEN, bool LOCAL, bool BSHD>
 hipError_t launch_tiles(const Params& p, const __bf16* dout, float* delta, float* lse2, __bf16* dq, __bf16* dk,
-                        __bf16* dv, hipStream_t st) {
-  // dense non-causal grids are padded to a multiple of 8 for the XCD
-  // mapping; varlen grids cover an upper bound of the tiles per head
-  // (T / tile + sequences), the surplus items exit at once.  LOCAL (a
-  // sliding window) is causal.
+                        __bf16* dv, float* dsinks, hipStream_t st) {
+  // dQ first: it also forms Delta and the log2 LSE of every row, which the
+  // sink gradient and the dK/dV kernel read.  Dense non-causal grids are
+  // padded to a multiple of 8 for the XCD mapping; varlen grids cover an
+  // upper bound of the tiles per head (T / tile + sequences), the surplus
+  // items exit at once.  LOCAL (a sliding window) is causal.
   auto pad8 = [](long n) { return (n + 7) / 8 * 8; };
   Params q = p;
+  long g2;
+  if (VARLEN) {
+    q.tiles_per_head = p.Sq / 128 + p.B;
+    g2 = (long)p.H * q.tiles_per_head;
+  } else {
+    g2 = (long)p.B * p.H * ceil_div(p.Sq, 128);
+    if (!p.causal) g2 = pad8(g2);
+  }
+  if (LOCAL)
+    hipLaunchKernelGGL((dq_kernel<D, true, VARLEN, true, BSHD>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta,
+                       lse2, dq);
+  else if (p.causal)
+    hipLaunchKernelGGL((dq_kernel<D, true, VARLEN, false, BSHD>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta,
+                       lse2, dq);
+  else
+    hipLaunchKernelGGL((dq_kernel<D, false, VARLEN, false, BSHD>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta,
+                       lse2, dq);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.sinks != nullptr) {
+    hipLaunchKernelGGL(dsink_kernel, dim3((unsigned)p.H), dim3(256), 0, st, p.sinks, (const float*)delta,
+                       (const float*)lse2, dsinks, VARLEN ? 1 : p.B, p.H, p.Sq);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (p.Skv > 0) {
     long g1;
     if (VARLEN) {
@@ -764,71 +787,36 @@ hipError_t launch_tiles(const Params& p, const __bf16* dout, float* delta, float
       if (!p.causal) g1 = pad8(g1);
     }
     if (LOCAL)
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, true, VARLEN, true, BSHD>), dim3((unsigned)g1), dim3(512), 0, st, q, dout,
-                         delta, lse2, dk, dv);
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, true, VARLEN, true, BSHD>), dim3((unsigned)g1), dim3(512), 0, st, q,
+                         dout, delta, lse2, dk, dv);
     else if (p.causal)
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, true, VARLEN, false, BSHD>), dim3((unsigned)g1), dim3(512), 0, st, q, dout,
-                         delta, lse2, dk, dv);
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, true, VARLEN, false, BSHD>), dim3((unsigned)g1), dim3(512), 0, st, q,
+                         dout, delta, lse2, dk, dv);
     else
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, false, VARLEN, false, BSHD>), dim3((unsigned)g1), dim3(512), 0, st, q, dout,
-                         delta, lse2, dk, dv);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, false, VARLEN, false, BSHD>), dim3((unsigned)g1), dim3(512), 0, st, q,
+                         dout, delta, lse2, dk, dv);
+    e = hipGetLastError();
   }
-  long g2;
-  if (VARLEN) {
-    q.tiles_per_head = p.Sq / 128 + p.B;
-    g2 = (long)p.H * q.tiles_per_head;
-  } else {
-    g2 = (long)p.B * p.H * ceil_div(p.Sq, 128);
-    if (!p.causal) g2 = pad8(g2);
-  }
-  if (LOCAL)
-    hipLaunchKernelGGL((dq_kernel<D, true, VARLEN, true, BSHD>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta, lse2,
-                       dq);
-  else if (p.causal)
-    hipLaunchKernelGGL((dq_kernel<D, true, VARLEN, false, BSHD>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta,
-                       lse2, dq);
-  else
-    hipLaunchKernelGGL((dq_kernel<D, false, VARLEN, false, BSHD>), dim3((unsigned)g2), dim3(256), 0, st, q, dout, delta,
-                       lse2, dq);
-  return hipGetLastError();
+  return e;
 }
 
 template <int D>
 hipError_t launch_bwd_d(const Params& p, const __bf16* dout, float* delta, float* lse2, __bf16* dq, __bf16* dk,
                         __bf16* dv, float* dsinks, hipStream_t st) {
   const bool var = p.cu != nullptr;
-  const int nb = var ? 1 : p.B;
-  const long rows = (long)nb * p.H * p.Sq;
-  constexpr int RPB = 256 / (D / 8);
-  if (p.bshd)
-    hipLaunchKernelGGL((delta_kernel<D, true>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
-                       (const __bf16*)p.o, dout, p.lse, delta, lse2, rows, p.H, p.Sq);
-  else
-    hipLaunchKernelGGL((delta_kernel<D, false>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
-                       (const __bf16*)p.o, dout, p.lse, delta, lse2, rows, p.H, p.Sq);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (p.sinks != nullptr) {
-    hipLaunchKernelGGL(dsink_kernel, dim3((unsigned)p.H), dim3(256), 0, st, p.sinks, (const float*)delta,
-                       (const float*)lse2, dsinks, nb, p.H, p.Sq);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const bool local = p.window > 0;
   if (p.bshd) {
     if (var)
-      return local ? launch_tiles<D, true, true, true>(p, dout, delta, lse2, dq, dk, dv, st)
-                   : launch_tiles<D, true, false, true>(p, dout, delta, lse2, dq, dk, dv, st);
-    return local ? launch_tiles<D, false, true, true>(p, dout, delta, lse2, dq, dk, dv, st)
-                 : launch_tiles<D, false, false, true>(p, dout, delta, lse2, dq, dk, dv, st);
+      return local ? launch_tiles<D, true, true, true>(p, dout, delta, lse2, dq, dk, dv, dsinks, st)
+                   : launch_tiles<D, true, false, true>(p, dout, delta, lse2, dq, dk, dv, dsinks, st);
+    return local ? launch_tiles<D, false, true, true>(p, dout, delta, lse2, dq, dk, dv, dsinks, st)
+                 : launch_tiles<D, false, false, true>(p, dout, delta, lse2, dq, dk, dv, dsinks, st);
   }
   if (var)
-    return local ? launch_tiles<D, true, true, false>(p, dout, delta, lse2, dq, dk, dv, st)
-                 : launch_tiles<D, true, false, false>(p, dout, delta, lse2, dq, dk, dv, st);
-  return local ? launch_tiles<D, false, true, false>(p, dout, delta, lse2, dq, dk, dv, st)
-               : launch_tiles<D, false, false, false>(p, dout, delta, lse2, dq, dk, dv, st);
+    return local ? launch_tiles<D, true, true, false>(p, dout, delta, lse2, dq, dk, dv, dsinks, st)
+                 : launch_tiles<D, true, false, false>(p, dout, delta, lse2, dq, dk, dv, dsinks, st);
+  return local ? launch_tiles<D, false, true, false>(p, dout, delta, lse2, dq, dk, dv, dsinks, st)
+               : launch_tiles<D, false, false, false>(p, dout, delta, lse2, dq, dk, dv, dsinks, st);
 }
 
 }  // namespace
