@@ -1,4 +1,6 @@
-"""The compiled prefill kernel keeps its matrix-phase operand pipeline.
+"""The compiled kernels keep the code shape they were tuned for: the
+prefill kernel's matrix-phase operand pipeline, and no register spills in
+any prefill or backward kernel beyond the few bytes listed below.
 
 The steady matrix phase of the ping-pong prefill kernel issues 32 MFMAs,
 each with its A operand (a K or V fragment) read from LDS a few MFMAs
@@ -74,3 +76,46 @@ def test_matrix_phase_operand_ring(prefill_asm):
                 "(the operand reads are no longer issued ahead of the MFMAs)")
             checked += 1
     assert checked >= 48, checked  # several steady matrix phases per instantiation
+
+
+def _scratch(asm: str):
+    """Private (scratch) bytes per kernel from the code object metadata."""
+    out = {}
+    for block in asm.split("- .agpr_count:")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block)
+        size = re.search(r"\.private_segment_fixed_size:\s+(\d+)", block)
+        if name and size:
+            out[name.group(1)] = int(size.group(1))
+    return out
+
+
+@pytest.fixture(scope="module")
+def backward_asm():
+    try:
+        cc = b.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    src = os.path.join(ROOT, "exact_attention_09_amd", "csrc", "attn_backward.hip")
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "bwd.s")
+        cmd = [cc, *[f for f in b.FLAGS if f != "-fPIC"], "--cuda-device-only", "-S", src, "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        return open(out).read()
+
+
+def test_no_register_spills(prefill_asm, backward_asm):
+    """Every prefill and backward kernel keeps its values in registers: a
+    spill to scratch memory in a tile loop has cost 4-70 % before.  A few
+    instantiations are allowed the bytes they have long had, none of them in
+    a tile loop: the packed-sequence d = 128 prefill kernels (12 bytes: two
+    values stored at setup and reloaded once per item, in the item lookup)
+    and the windowed d = 128 dQ kernels (one value outside the key-tile
+    loop; in the packed-sequence one, one 8-byte reload per tile)."""
+    spills = {**_scratch(prefill_asm), **_scratch(backward_asm)}
+    assert len(spills) >= 24 + 24, f"kernels found: {len(spills)}"
+    allowed = {"prefill_pp_kernelILi128ELb1ELb1ELb0E": 12, "prefill_pp_kernelILi128ELb0ELb1ELb0E": 12,
+               "dq_kernelILi128ELb1ELb0ELb1E": 8, "dq_kernelILi128ELb1ELb1ELb1E": 16}
+    for name, size in spills.items():
+        limit = next((v for k, v in allowed.items() if k in name), 0)
+        assert size <= limit, f"{name}: {size} bytes of scratch (allowed {limit})"
