@@ -248,3 +248,55 @@ def test_random_paged_decode(c):
     a_ref, _ = paged_oracle.paged_attention(q32[:, :, 0], k32, np.abs(v32), table, seqlens, scale)
     check(o.float().cpu().numpy()[:, :, 0], lse.cpu().numpy(), o_ref, lse_ref, "bf16", f"random {name_paged(c)}",
           a_ref=a_ref)
+
+
+# ---- many short sequences: the paths past the persistent grid's limit (more
+# than 1024 sequences, forward) and past the ranked backward order (more than
+# 64 sequences)
+
+MANY = [
+    # (layout, sequences, max length, H, Hkv, d, causal, backward)
+    ("bshd", 1100, 24, 2, 1, 128, True, False),
+    ("bhsd", 1100, 24, 4, 2, 64, False, False),
+    ("bshd", 100, 90, 2, 1, 128, True, True),
+    ("bhsd", 100, 90, 4, 4, 64, False, True),
+]
+
+
+@pytest.mark.parametrize("c", MANY, ids=lambda c: "-".join(map(str, c)))
+def test_many_sequences(c):
+    import exact_attention_09_amd as ea
+    layout, nseq, maxlen, H, Hkv, d, causal, backward = c
+    say(f"many sequences {c}")
+    rng = np.random.default_rng(nseq * 7 + maxlen)
+    lengths = tuple(int(x) for x in rng.integers(0, maxlen + 1, nseq))
+    cfg = dict(layout=layout, d=d, H=H, Hkv=Hkv, causal=causal, window=0, sinks=False, lengths=lengths, B=nseq,
+               Sq=sum(lengths), Skv=sum(lengths))
+    seed = 10 * (MANY.index(c) + 9900)
+    (q, k, v, do), _, (qt, kt, vt, dot), cu, cut, _ = inputs(cfg, seed)
+    o, lse = ea.attn_fwd_layout(qt, kt, vt, layout=layout, causal=causal, cu_seqlens=cut)
+    hq, hk, hv = (host_f32(x, "bf16") for x in (q, k, v))
+    scale = 1.0 / math.sqrt(d)
+    if not backward:
+        torch.cuda.synchronize()
+        og = to_bhsd(o, cfg)
+        lg = lse.cpu().numpy().astype(np.float64).reshape(og.shape[:-1])
+        o_ref, lse_ref, a_ref = reference(hq, hk, hv, scale, causal, cu_seqlens=cu)
+        check(og, lg, o_ref, lse_ref, "bf16", f"many sequences {c}", a_ref=a_ref)
+        return
+    dq, dk, dv, _ = ea.attn_bwd_layout(qt, kt, vt, o, lse, dot, layout=layout, causal=causal, cu_seqlens=cut)
+    torch.cuda.synchronize()
+    got = tuple(to_bhsd(t, cfg) for t in (dq, dk, dv))
+    hdo = host_f32(do, "bf16")
+    for i in range(nseq):
+        a, e = int(cu[i]), int(cu[i + 1])
+        if e == a:
+            continue
+        sl = slice(a, e)
+        want = bwd_oracle.attention_backward(hq[:, :, sl], hk[:, :, sl], hv[:, :, sl], hdo[:, :, sl], scale, causal)
+        for g, w, name in zip(got, want[:3], ("dq", "dk", "dv")):
+            gs = g[:, :, sl]
+            scale_w = max(np.abs(w).max(), 1e-30)
+            err = np.abs(gs - w).max()
+            assert err <= 1e-2 * scale_w + 1e-4, f"{c} sequence {i} {name}: max|err| {err:.3g} of {scale_w:.3g}"
+    say(f"  many sequences {c}: {nseq} sequences within the backward bar")
